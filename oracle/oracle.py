@@ -1,0 +1,363 @@
+"""CPU oracle of the DSA lightning-indexer hot path (test infrastructure).
+
+Each function restates one step the pages describe, in the order the indexer
+runs them:
+
+1. ``geometry``    - packed (THD) documents from ``cu_seqlens``; causal keys are
+                     the keys of the query's own document at or before it.
+2. ``preprocess``  - key LayerNorm then RoPE, in fp32, with or without the bf16
+                     round-trip (PR 8403, "What does this PR do?" and
+                     "Motivation": the default path materialises BF16 between the
+                     key LayerNorm and RoPE; ``dsa_indexer_rope_fp32`` keeps the
+                     chain in FP32).
+3. ``quantize``    - scoring operands: bf16 (round to nearest even, also for fp32
+                     carriers: PR 8403, codex review finding 2), FP8 E4M3 with a
+                     UE8M0 scale per vector (PR 8403, "What does this PR do?"), or
+                     MXFP8 with a UE8M0 scale per 32 elements (PR 5992, "Key
+                     changes").
+4. ``kpool``       - pooled keys: per document, each complete group of kpool
+                     tokens is compressed with a softmax over a bf16 per-token gate
+                     plus an fp32 per-slot bias (PR 7522, "Changes").
+5. ``score_rows``  - I[t,c] = sm_scale * sum_h w[t,h] * ReLU(q[t,h,:] . k[c,:]) over
+                     the causal candidates c of t, in fp64 on the exactly
+                     dequantised operands, with the forward-error scale
+                     M[t,c] = |sm_scale| * sum_h |w[t,h]| * sum_i |q[t,h,i] k[c,i]|.
+                     (Scoring call with per-head weights, ``ratio`` 1 and
+                     ``sm_scale``: PR 8403, codex review finding 3; ReLU scoring:
+                     finding 1.)
+6. ``topk_row``    - the min(topk, cand) best candidates, ordered by score
+                     descending then index ascending; the deterministic tie rule
+                     gives the lower index (PR 5992, "Key changes": deterministic
+                     top-k tie breaking). Padding is index -1 / score -inf.
+7. ``expand``      - selected pools back to token indices, plus the query's
+                     incomplete causal pool when the tail option is on
+                     (PR 7522, "Changes").
+
+Everything is plain numpy; there is no blocking beyond splitting rows into
+groups so that one matmul fits in memory.
+"""
+
+import numpy as np
+
+from . import formats as fm
+
+F32 = np.float32
+F64 = np.float64
+
+PRECISIONS = ("bf16", "fp8", "mxfp8")
+MX_BLOCK = 32
+
+
+# --------------------------------------------------------------------------
+# 1. Geometry
+# --------------------------------------------------------------------------
+
+def check_cu_seqlens(cu_seqlens, T):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    return cu
+
+
+def geometry(cu_seqlens, T):
+    """Document id and position inside the document of every token 0..T-1."""
+    cu = check_cu_seqlens(cu_seqlens, T)
+    t = np.arange(T, dtype=np.int64)
+    doc = np.searchsorted(cu, t, side="right") - 1
+    return doc, t - cu[doc]
+
+
+def pool_offsets(cu_seqlens, kp):
+    """cu_pools[b] = number of complete pools in documents before b."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = np.diff(cu) // kp
+    return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+
+
+def candidate_count(pos, kp):
+    """Causal candidates of a query at position u: u+1 tokens, or floor((u+1)/kp) whole pools."""
+    return (np.asarray(pos, dtype=np.int64) + 1) // kp
+
+
+# --------------------------------------------------------------------------
+# 2. Preprocess: key LayerNorm, then RoPE (fp32)
+# --------------------------------------------------------------------------
+
+def tree_sum32(a):
+    """Pinned fp32 halving sum over the last axis (length a power of two).
+
+    For n = D/2, D/4, ..., 1: a[i] <- a[i] + a[i+n] for i < n; the result is a[0].
+    """
+    a = np.array(a, dtype=F32, copy=True)
+    n = a.shape[-1] // 2
+    while n >= 1:
+        a[..., :n] = a[..., :n] + a[..., n:2 * n]
+        n //= 2
+    return a[..., 0]
+
+
+def key_layernorm(x, gamma, beta, eps):
+    """LayerNorm over the last axis in fp32, each operation rounded on its own.
+
+    mean = tree(x) * (1/D); d = x - mean; var = tree(d*d) * (1/D) (biased);
+    rstd = 1 / sqrt(var + eps); y = (d * rstd) * gamma + beta.
+    """
+    x = np.asarray(x, dtype=F32)
+    D = x.shape[-1]
+    if D & (D - 1):
+        raise ValueError("LayerNorm width must be a power of two")
+    inv_d = F32(1.0 / D)
+    mean = tree_sum32(x) * inv_d
+    d = x - mean[..., None]
+    var = tree_sum32(d * d) * inv_d
+    rstd = F32(1.0) / np.sqrt(var + F32(eps))
+    y = (d * rstd[..., None]) * np.asarray(gamma, dtype=F32)
+    return (y + np.asarray(beta, dtype=F32)).astype(F32)
+
+
+def rope_pairs(D, rope_dim, interleaved):
+    """Index pairs (i1, i2) rotated together inside the last ``rope_dim`` dims."""
+    base = D - rope_dim
+    j = np.arange(rope_dim // 2)
+    if interleaved:
+        return base + 2 * j, base + 2 * j + 1
+    return base + j, base + rope_dim // 2 + j
+
+
+def rope(x, pos, cos, sin, rope_dim, interleaved=False):
+    """Rotary embedding on the last ``rope_dim`` dims, fp32, no fused multiply-add.
+
+    Pair (i1, i2) with angle table column j at position u:
+    y1 = x1*c - x2*s, y2 = x2*c + x1*s (every product and sum rounded to fp32).
+    """
+    x = np.array(x, dtype=F32, copy=True)
+    if rope_dim == 0:
+        return x
+    i1, i2 = rope_pairs(x.shape[-1], rope_dim, interleaved)
+    c = np.asarray(cos, dtype=F32)[pos]
+    s = np.asarray(sin, dtype=F32)[pos]
+    x1 = x[..., i1].copy()
+    x2 = x[..., i2].copy()
+    x[..., i1] = x1 * c - x2 * s
+    x[..., i2] = x2 * c + x1 * s
+    return x
+
+
+def preprocess(q_in, k_in, cu_seqlens, gamma=None, beta=None, eps=1e-6,
+               cos=None, sin=None, rope_dim=0, interleaved=False, rope_fp32=False):
+    """fp32 carriers of q [T,H,D] and k [S,D] before quantisation.
+
+    ``q_in`` and ``k_in`` are the input values widened to fp32. Keys get the
+    LayerNorm (if ``gamma`` is given) and then RoPE; queries get RoPE only.
+    Positions restart at every document. With ``rope_fp32`` off every carrier
+    handed from one step to the next is bf16: the input of RoPE and its output
+    are rounded to bf16. With it on the carrier stays fp32 up to quantisation.
+    """
+    q = np.asarray(q_in, dtype=F32)
+    k = np.asarray(k_in, dtype=F32)
+    T, S = q.shape[0], k.shape[0]
+    if T != S:
+        raise ValueError("queries and keys share one cu_seqlens (T == S)")
+    _, pos = geometry(cu_seqlens, T)
+    rnd = (lambda v: v) if rope_fp32 else fm.bf16_round
+
+    y = key_layernorm(k, gamma, beta, eps) if gamma is not None else k
+    y = rnd(y)
+    if rope_dim:
+        y = rnd(rope(y, pos, cos, sin, rope_dim, interleaved))
+    k_car = y
+
+    y = rnd(q)
+    if rope_dim:
+        y = rnd(rope(y, pos[:, None], cos, sin, rope_dim, interleaved))
+    return y.astype(F32), k_car.astype(F32)
+
+
+# --------------------------------------------------------------------------
+# 3. Scoring operands
+# --------------------------------------------------------------------------
+
+def quantize(carrier, precision):
+    """(operand, scale) of an fp32 carrier [..., D].
+
+    bf16: uint16 bits, no scale. fp8: E4M3FN codes + one UE8M0 code per vector
+    ([...]). mxfp8: E4M3FN codes + one UE8M0 code per 32 elements ([..., D/32]).
+    """
+    x = np.asarray(carrier, dtype=F32)
+    if precision == "bf16":
+        return fm.bf16_bits(x), None
+    if precision == "fp8":
+        codes, sc = fm.quantize_fp8_blocks(x, x.shape[-1])
+        return codes, sc[..., 0]
+    if precision == "mxfp8":
+        return fm.quantize_fp8_blocks(x, MX_BLOCK)
+    raise ValueError(f"unsupported scoring precision {precision!r}; expected bf16, fp8 or mxfp8")
+
+
+def dequantize(op, scale, precision):
+    """Exact float64 value of a scoring operand."""
+    if precision == "bf16":
+        return fm.bf16_to_f32(op).astype(F64)
+    if precision == "fp8":
+        return fm.dequantize_fp8_blocks(op, np.asarray(scale)[..., None], np.asarray(op).shape[-1])
+    if precision == "mxfp8":
+        return fm.dequantize_fp8_blocks(op, scale, MX_BLOCK)
+    raise ValueError(f"unsupported scoring precision {precision!r}")
+
+
+# --------------------------------------------------------------------------
+# 4. KPool compression
+# --------------------------------------------------------------------------
+
+def kpool(k, cu_seqlens, gate_bits, bias, kp):
+    """Pooled keys (fp32) [P, D] and cu_pools [B+1].
+
+    Per document, pool p holds tokens cu[b] + p*kp + j, j < kp; only complete
+    pools exist. With z_j = gate_j + bias_j (fp32), m = max_j z_j,
+    e_j = pexp(z_j - m), sigma = e_0 + e_1 + ... (left to right),
+    a_j = e_j / sigma, the pooled key is a_0*k_0 + a_1*k_1 + ... accumulated left
+    to right in fp32, each product and each sum rounded.
+    """
+    k = np.asarray(k, dtype=F32)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cu_pools = pool_offsets(cu, kp)
+    starts = np.concatenate([cu[b] + kp * np.arange((cu[b + 1] - cu[b]) // kp)
+                             for b in range(cu.size - 1)] + [np.zeros(0, np.int64)]).astype(np.int64)
+    P, D = starts.size, k.shape[1]
+    if P == 0:
+        return np.zeros((0, D), F32), cu_pools
+    tok = starts[:, None] + np.arange(kp)[None, :]                        # [P, kp]
+    g = fm.bf16_to_f32(np.asarray(gate_bits, dtype=np.uint16)[tok])
+    z = g + np.asarray(bias, dtype=F32)[None, :]
+    m = np.max(z, axis=1)
+    e = fm.pexp(z - m[:, None])
+    sigma = e[:, 0].copy()
+    for j in range(1, kp):
+        sigma = sigma + e[:, j]
+    a = e / sigma[:, None]
+    acc = a[:, 0:1] * k[tok[:, 0]]
+    for j in range(1, kp):
+        acc = acc + a[:, j:j + 1] * k[tok[:, j]]
+    return acc.astype(F32), cu_pools
+
+
+# --------------------------------------------------------------------------
+# 5. Scores
+# --------------------------------------------------------------------------
+
+def score_rows(q, k, w, cu_seqlens, sm_scale=1.0, kp=1, cu_pools=None, rows=None,
+               block_elems=1 << 24):
+    """Exact-operand fp64 scores of the causal candidates of the given query rows.
+
+    q [T,H,D], k [Sk,D] and w [T,H] are float64 values (dequantised operands).
+    Returns {t: (I, M)} where I[c], M[c] are over candidates c = 0..cand(t)-1
+    (document-local key or pool index).
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    w = np.asarray(w, dtype=F64)
+    T, H, D = q.shape
+    doc, pos = geometry(cu_seqlens, T)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    base = cu if kp == 1 else np.asarray(cu_pools, dtype=np.int64)
+    cand = candidate_count(pos, kp)
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = {}
+    order = rows[np.lexsort((rows, doc[rows]))]
+    i = 0
+    while i < order.size:
+        b = doc[order[i]]
+        j = i
+        ext = 0
+        while j < order.size and doc[order[j]] == b:
+            ext_j = max(ext, int(cand[order[j]]))
+            if (j - i + 1) * H * max(ext_j, 1) > block_elems and j > i:
+                break
+            ext = ext_j
+            j += 1
+        blk = order[i:j]
+        kd = k[base[b]:base[b] + ext]
+        qb = q[blk].reshape(-1, D)
+        logits = (qb @ kd.T).reshape(blk.size, H, ext)
+        absl = (np.abs(qb) @ np.abs(kd).T).reshape(blk.size, H, ext)
+        wb = w[blk][:, :, None]
+        I = sm_scale * np.sum(wb * np.maximum(logits, 0.0), axis=1)
+        M = abs(sm_scale) * np.sum(np.abs(wb) * absl, axis=1)
+        for r, t in enumerate(blk):
+            n = int(cand[t])
+            out[int(t)] = (I[r, :n].copy(), M[r, :n].copy())
+        i = j
+    return out
+
+
+# --------------------------------------------------------------------------
+# 6. Top-k and 7. expansion
+# --------------------------------------------------------------------------
+
+def topk_row(I, topk):
+    """Local indices and scores of the min(topk, cand) best candidates, ordered by
+    (score descending, index ascending)."""
+    I = np.asarray(I, dtype=F64)
+    order = np.lexsort((np.arange(I.size), -I))
+    sel = order[:min(topk, I.size)]
+    return sel.astype(np.int64), I[sel]
+
+
+def expand(pool_local, pos, kp, doc_start, tail):
+    """Token indices of selected pools (in selection order, each ascending), then the tail.
+
+    The tail is the query's incomplete causal pool, tokens from the start of the
+    pool holding position ``pos`` up to ``pos`` itself; it exists only when
+    (pos+1) is not a multiple of kp.
+    """
+    toks = [doc_start + p * kp + np.arange(kp) for p in np.asarray(pool_local, dtype=np.int64)]
+    if tail and (pos + 1) % kp != 0:
+        toks.append(doc_start + (pos // kp) * kp + np.arange((pos + 1) % kp))
+    if not toks:
+        return np.zeros(0, np.int64)
+    return np.concatenate(toks).astype(np.int64)
+
+
+def index_topk(q, k, w, cu_seqlens, topk, sm_scale=1.0, kp=1, cu_pools=None,
+               kpool_tail=True, rows=None):
+    """Full selection for the given rows (all by default) from float64 operand values.
+
+    Returns a dict of per-row results: 'I', 'M' (candidate scores and error
+    scales), 'sel' (local ids), 'indices' (global key row, or global pool row),
+    'scores', 'length', and for kp > 1 'tokens' (expanded token indices).
+    """
+    T = np.asarray(q).shape[0]
+    doc, pos = geometry(cu_seqlens, T)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    base = cu if kp == 1 else np.asarray(cu_pools, dtype=np.int64)
+    sc = score_rows(q, k, w, cu_seqlens, sm_scale, kp, cu_pools, rows)
+    res = {}
+    for t, (I, M) in sc.items():
+        b = doc[t]
+        sel, s = topk_row(I, topk)
+        r = {"I": I, "M": M, "sel": sel, "indices": base[b] + sel, "scores": s}
+        if kp == 1:
+            r["length"] = sel.size
+        else:
+            toks = expand(sel, int(pos[t]), kp, int(cu[b]), kpool_tail)
+            r["tokens"] = toks
+            r["length"] = toks.size
+        res[t] = r
+    return res
+
+
+def dense_outputs(res, T, topk, kp=1):
+    """Padded arrays (indices -1 / scores -inf) from ``index_topk`` results."""
+    idx = np.full((T, topk), -1, np.int64)
+    scr = np.full((T, topk), -np.inf)
+    lng = np.zeros(T, np.int64)
+    width = topk * kp + kp - 1
+    tok = np.full((T, width), -1, np.int64) if kp > 1 else None
+    for t, r in res.items():
+        n = r["sel"].size
+        idx[t, :n] = r["indices"]
+        scr[t, :n] = r["scores"]
+        lng[t] = r["length"]
+        if kp > 1:
+            tok[t, :r["tokens"].size] = r["tokens"]
+    return idx, scr, lng, tok
