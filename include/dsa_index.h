@@ -1,0 +1,207 @@
+/*
+ * dsa_index.h - C ABI of the DSA lightning-indexer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The indexer of DeepSeek Sparse Attention scores, for every query token t and
+ * every causal key c of t's document,
+ *
+ *     I[t,c] = sm_scale * sum_h w[t,h] * ReLU(q[t,h,:] . k[c,:])
+ *
+ * and keeps the `topk` best keys per query. Sources (Megatron-LM pull requests):
+ *   - PR 8403 ("What does this PR do?", "Implementation", codex review findings 1-3):
+ *     the single scoring call taking q, k, per-head weights w, ratio and sm_scale; ReLU
+ *     scoring; key LayerNorm then RoPE kept in FP32 (`dsa_indexer_rope_fp32`); BF16
+ *     or FP8 (E4M3 with UE8M0 per-vector scales) scoring precision; an unknown
+ *     precision is a ValueError; the (indices, lengths, scores) outputs.
+ *   - PR 5992 ("[dev] [DeepSeek-V4] Add compact BF16 and MXFP8 DSA indexer support",
+ *     "Key changes" and review summaries): MXFP8 scoring, caller-owned workspaces that
+ *     are safe under graph capture, live cu_seqlens read on every call, deterministic
+ *     top-k tie breaking.
+ *   - PR 7522 ("Changes"): KPool pooled keys (BF16 per-token gate, FP32 per-slot bias),
+ *     selection over pools expanded back to token indices, the incomplete causal tail
+ *     pool, pooling restarting at document boundaries, the NoPE indexer.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; all arrays are dense and
+ *     row-major with the last dimension contiguous. Scalars are host values.
+ *   - Queries and keys are packed (THD): documents b = 0..num_seqs-1 occupy rows
+ *     cu_seqlens[b] .. cu_seqlens[b+1]-1. cu_seqlens is int32 [num_seqs+1] in device
+ *     memory with cu_seqlens[0] = 0, non-decreasing, last entry = T. It is read on the
+ *     device on every call, so it may change between graph capture and replay.
+ *     Positions (for RoPE) restart at 0 in every document. Query t's causal keys are
+ *     the keys of its own document at positions 0..u (u = t's position), that is
+ *     global key rows cu_seqlens[b] .. t.
+ *   - The library never allocates, frees or synchronises the host inside a call. All
+ *     work is enqueued on `stream` (asynchronous); results are ready when the stream is.
+ *   - Device-side data is trusted but never read out of bounds: a malformed cu_seqlens
+ *     is clamped to [0, T] and documents longer than `max_seqlen` are truncated to it
+ *     (their later rows see at most max_seqlen candidates); results are then unspecified.
+ *   - Every entry point returns a status. Host-side validation runs before anything is
+ *     enqueued; on a non-OK status nothing was enqueued unless the status is
+ *     DSA_ERR_DEVICE. dsa_last_error() describes the last non-OK status of the calling
+ *     thread.
+ *   - Results are deterministic: identical inputs give byte-identical outputs on every
+ *     call and stream (no floating-point atomics, fixed reduction orders).
+ */
+#ifndef DSA_INDEX_H
+#define DSA_INDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,   /* NULL/misaligned pointer, bad size, bad enum value */
+  DSA_ERR_UNSUPPORTED = 2,        /* valid but outside the supported matrix (precision, H, D, rope_dim, sizes) */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_DEVICE = 4              /* a HIP launch failed; dsa_last_error() carries the HIP message */
+} dsa_status_t;
+
+typedef enum {
+  DSA_PREC_BF16 = 0,   /* bf16 operands, round to nearest even from the fp32 carrier */
+  DSA_PREC_FP8 = 1,    /* OCP E4M3FN payload + one UE8M0 scale per D-vector */
+  DSA_PREC_MXFP8 = 2   /* OCP E4M3FN payload + one UE8M0 scale per 32 elements */
+} dsa_precision_t;
+
+typedef enum { DSA_DTYPE_BF16 = 0, DSA_DTYPE_FP32 = 1 } dsa_dtype_t;
+
+/*
+ * Scoring operand formats (the `q_op/k_op` and `*_scale` arrays below):
+ *   bf16 : uint16 bf16 bit patterns [.., D]; no scale array (pass NULL).
+ *   fp8  : uint8 E4M3FN codes [.., D]; scale = uint8 UE8M0 code per vector, value
+ *          2^(code-127); the exponent e is the smallest integer with amax <= 448 * 2^e
+ *          (e = 0 for an all-zero vector, clamped to [-127,127]), payload =
+ *          round-to-nearest-even E4M3FN of x * 2^-e (never saturates).
+ *   mxfp8: as fp8 but one scale per 32 consecutive elements: scale array [.., D/32].
+ */
+
+/*
+ * dsa_index_preprocess - key LayerNorm then RoPE in fp32, fused with quantisation to the
+ * scoring operands (PR 8403, "What does this PR do?", "Motivation", "Implementation";
+ * PR 5992, "Key changes" for MXFP8; PR 7522, "Changes" for NoPE).
+ *
+ *   q_in      [T,H,D] in_dtype, or NULL to skip queries (then q_op/q_scale/q_f32_out unused)
+ *   k_in      [S,D]   in_dtype, or NULL to skip keys. T == S when both are given; with one
+ *             of them NULL the other's row count must match cu_seqlens[num_seqs].
+ *   ln_gamma, ln_beta  fp32 [D] key LayerNorm affine (the effective gamma); gamma NULL =>
+ *             no LayerNorm; beta NULL => zero. LayerNorm: mean and biased variance over D
+ *             with a pinned pairwise halving sum, rstd = 1/sqrt(var + ln_eps), each fp32
+ *             operation rounded separately. Queries get no LayerNorm.
+ *   rope_cos, rope_sin fp32 [rope_max_pos, rope_dim/2]: angle table, row = position inside
+ *             the document. rope_dim = 0 => NoPE (tables unused, may be NULL).
+ *             RoPE rotates the last rope_dim dims: rotate-half pairs (j, j+rope_dim/2) when
+ *             rope_interleaved = 0 (rope_dim % 32 == 0 required), adjacent pairs (2j, 2j+1)
+ *             when 1 (rope_dim even). y1 = x1*c - x2*s, y2 = x2*c + x1*s, no fused
+ *             multiply-add. Positions >= rope_max_pos read the last table row.
+ *   rope_fp32 0 => default path: the input of RoPE and its output are rounded to bf16
+ *             (the "materialised BF16" round-trip); 1 => the fp32 carrier is kept up to
+ *             quantisation.
+ *   precision output operand format (see above).
+ *   q_op [T,H,D], q_scale ([T,H] fp8, [T,H,D/32] mxfp8, NULL for bf16),
+ *   k_op [S,D],   k_scale ([S] fp8, [S,D/32] mxfp8, NULL for bf16).
+ *   q_f32_out [T,H,D], k_f32_out [S,D]: optional fp32 carriers just before quantisation.
+ * Supported: H in {16,32,64}, D in {64,128}. Pointers: q_in/k_in/q_op/k_op and the fp32
+ * outputs 16-byte aligned.
+ */
+dsa_status_t dsa_index_preprocess(
+    const void* q_in, const void* k_in, dsa_dtype_t in_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs,
+    const float* ln_gamma, const float* ln_beta, float ln_eps,
+    const float* rope_cos, const float* rope_sin,
+    int32_t rope_dim, int32_t rope_max_pos, int32_t rope_interleaved,
+    int32_t rope_fp32, dsa_precision_t precision,
+    void* q_op, uint8_t* q_scale, void* k_op, uint8_t* k_scale,
+    float* q_f32_out, float* k_f32_out,
+    hipStream_t stream);
+
+/*
+ * dsa_index_kpool - KPool key compression (PR 7522, "Changes").
+ *
+ * Within each document, pool p holds tokens cu_seqlens[b] + p*kpool + j, j < kpool; only
+ * complete pools exist and pooling restarts at every document. With
+ * z_j = gate[token_j] + slot_bias[j] (fp32), m = max z, e_j = pexp(z_j - m),
+ * sigma = e_0 + e_1 + ... (left to right), a_j = e_j / sigma, the pooled key is
+ * a_0*k_0 + a_1*k_1 + ... accumulated left to right in fp32 (no fused multiply-add),
+ * then quantised to `precision`. pexp is a pinned exponential: 0 below -104, otherwise
+ * n = rint(z*log2e), r = fma(-n, ln2_lo, fma(-n, ln2_hi, z)) with ln2_hi = 0x3F317200,
+ * ln2_lo = 0x35BFBE8E, a degree-7 Taylor polynomial in r by Horner's rule with fused
+ * multiply-adds, scaled by 2^n.
+ *
+ *   k          [S,D] keys (raw or preprocessed carriers), k_dtype bf16 or fp32
+ *   gate_bf16  [S]   bf16 bit patterns, one compression logit per token
+ *   slot_bias  [kpool] fp32
+ *   kpool      2..64 (1 is accepted and copies the keys)
+ *   pooled_op  [floor(S/kpool), D] operand rows, pooled_scale as for keys (NULL for bf16);
+ *              only the first cu_pools[num_seqs] rows are written.
+ *   cu_pools   int32 [num_seqs+1] output: cu_pools[b] = complete pools in documents < b.
+ */
+dsa_status_t dsa_index_kpool(
+    const void* k, dsa_dtype_t k_dtype, int32_t S, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs,
+    const uint16_t* gate_bf16, const float* slot_bias, int32_t kpool,
+    dsa_precision_t precision,
+    void* pooled_op, uint8_t* pooled_scale, int32_t* cu_pools,
+    hipStream_t stream);
+
+/*
+ * dsa_index_workspace_size - bytes of caller-owned workspace dsa_index_score_topk needs.
+ * It holds the fp32 scores of every row's candidates at a fixed row stride (a multiple of
+ * 64 not below the largest candidate count, max_seqlen or max_seqlen/kpool) plus 256
+ * bytes. Pure host computation; returns 0 for invalid arguments.
+ */
+size_t dsa_index_workspace_size(int32_t T, int32_t H, int32_t D, int32_t num_seqs,
+                                int32_t max_seqlen, int32_t topk, int32_t kpool,
+                                dsa_precision_t precision);
+
+/*
+ * dsa_index_score_topk - scores of every causal candidate, then per-row top-k
+ * (PR 8403 codex review findings 1-3; PR 5992 "Key changes"; PR 7522 "Changes").
+ *
+ *   q_op, q_scale  [T,H,D] scoring operands (+ scales) as produced by dsa_index_preprocess
+ *   k_op, k_scale  [S,D] token keys (kpool == 1), or [S,D] pooled keys (kpool > 1, S = rows
+ *                  of pooled_op)
+ *   w              [T,H] per-head weights, fp32 or bf16 (w_dtype)
+ *   cu_seqlens     as above; max_seqlen is a static host upper bound of the document
+ *                  lengths (sizes the grid and the workspace)
+ *   kpool, cu_pools, kpool_tail: kpool > 1 scores pools: query t at position u sees the
+ *                  floor((u+1)/kpool) complete pools of its document (pooled row
+ *                  cu_pools[b] + p); kpool_tail != 0 appends its incomplete causal pool.
+ *   topk >= 1, sm_scale multiplies every score.
+ *   Outputs (all written in full, padding -1 / -inf):
+ *     out_scores [T,topk] fp32 - selected scores (pool scores when kpool > 1), ordered by
+ *                score descending then index ascending; ties go to the lower index.
+ *     out_indices: kpool == 1: [T,topk] int32 global key rows (cu_seqlens[b] + c).
+ *                  kpool  > 1: [T, topk*kpool + kpool - 1] int32 token indices: every
+ *                  selected pool's kpool tokens in ascending order, pools in selection
+ *                  order, then the tail tokens (pool start .. t).
+ *     out_lengths [T] int32: valid entries of out_indices (tokens when kpool > 1).
+ *     out_pool_indices [T,topk] int32 global pooled rows (kpool > 1), may be NULL.
+ *   workspace, workspace_bytes: device buffer of at least dsa_index_workspace_size(...)
+ *   bytes, 256-byte aligned. Its contents on entry do not matter.
+ * Supported: H in {16,32,64}, D in {64,128}; max_seqlen/kpool <= 32768 candidates per row.
+ */
+dsa_status_t dsa_index_score_topk(
+    const void* q_op, const uint8_t* q_scale,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools, int32_t kpool_tail,
+    int32_t topk, float sm_scale, dsa_precision_t precision,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths,
+    int32_t* out_pool_indices,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEX_H */

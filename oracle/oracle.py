@@ -144,7 +144,7 @@ def rope(x, pos, cos, sin, rope_dim, interleaved=False):
 
 
 def preprocess(q_in, k_in, cu_seqlens, gamma=None, beta=None, eps=1e-6,
-               cos=None, sin=None, rope_dim=0, interleaved=False, rope_fp32=False):
+               cos=None, sin=None, rope_dim=0, interleaved=False, rope_fp32=False, q_rows=None):
     """fp32 carriers of q [T,H,D] and k [S,D] before quantisation.
 
     ``q_in`` and ``k_in`` are the input values widened to fp32. Keys get the
@@ -152,13 +152,16 @@ def preprocess(q_in, k_in, cu_seqlens, gamma=None, beta=None, eps=1e-6,
     Positions restart at every document. With ``rope_fp32`` off every carrier
     handed from one step to the next is bf16: the input of RoPE and its output
     are rounded to bf16. With it on the carrier stays fp32 up to quantisation.
+    ``q_rows`` (optional) names the token rows ``q_in`` holds, for sampled checks.
     """
     q = np.asarray(q_in, dtype=F32)
     k = np.asarray(k_in, dtype=F32)
-    T, S = q.shape[0], k.shape[0]
+    S = k.shape[0]
+    T = S if q_rows is not None else q.shape[0]
     if T != S:
         raise ValueError("queries and keys share one cu_seqlens (T == S)")
-    _, pos = geometry(cu_seqlens, T)
+    _, pos_all = geometry(cu_seqlens, T)
+    pos = pos_all
     rnd = (lambda v: v) if rope_fp32 else fm.bf16_round
 
     y = key_layernorm(k, gamma, beta, eps) if gamma is not None else k
@@ -167,9 +170,10 @@ def preprocess(q_in, k_in, cu_seqlens, gamma=None, beta=None, eps=1e-6,
         y = rnd(rope(y, pos, cos, sin, rope_dim, interleaved))
     k_car = y
 
+    qpos = pos_all if q_rows is None else pos_all[np.asarray(q_rows, dtype=np.int64)]
     y = rnd(q)
     if rope_dim:
-        y = rnd(rope(y, pos[:, None], cos, sin, rope_dim, interleaved))
+        y = rnd(rope(y, qpos[:, None], cos, sin, rope_dim, interleaved))
     return y.astype(F32), k_car.astype(F32)
 
 
@@ -249,14 +253,14 @@ def score_rows(q, k, w, cu_seqlens, sm_scale=1.0, kp=1, cu_pools=None, rows=None
                block_elems=1 << 24):
     """Exact-operand fp64 scores of the causal candidates of the given query rows.
 
-    q [T,H,D], k [Sk,D] and w [T,H] are float64 values (dequantised operands).
-    Returns {t: (I, M)} where I[c], M[c] are over candidates c = 0..cand(t)-1
-    (document-local key or pool index).
+    q [T,H,D] (or a mapping from row t to its [H,D] values), k [Sk,D] and w [T,H] are
+    float64 values (dequantised operands). Returns {t: (I, M)} where I[c], M[c] are over
+    candidates c = 0..cand(t)-1 (document-local key or pool index).
     """
-    q = np.asarray(q, dtype=F64)
     k = np.asarray(k, dtype=F64)
     w = np.asarray(w, dtype=F64)
-    T, H, D = q.shape
+    T, H = w.shape
+    D = k.shape[1]
     doc, pos = geometry(cu_seqlens, T)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     base = cu if kp == 1 else np.asarray(cu_pools, dtype=np.int64)
@@ -277,7 +281,7 @@ def score_rows(q, k, w, cu_seqlens, sm_scale=1.0, kp=1, cu_pools=None, rows=None
             j += 1
         blk = order[i:j]
         kd = k[base[b]:base[b] + ext]
-        qb = q[blk].reshape(-1, D)
+        qb = np.stack([np.asarray(q[int(t)], dtype=F64) for t in blk]).reshape(-1, D)
         logits = (qb @ kd.T).reshape(blk.size, H, ext)
         absl = (np.abs(qb) @ np.abs(kd).T).reshape(blk.size, H, ext)
         wb = w[blk][:, :, None]
@@ -326,7 +330,7 @@ def index_topk(q, k, w, cu_seqlens, topk, sm_scale=1.0, kp=1, cu_pools=None,
     scales), 'sel' (local ids), 'indices' (global key row, or global pool row),
     'scores', 'length', and for kp > 1 'tokens' (expanded token indices).
     """
-    T = np.asarray(q).shape[0]
+    T = np.asarray(w).shape[0]
     doc, pos = geometry(cu_seqlens, T)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     base = cu if kp == 1 else np.asarray(cu_pools, dtype=np.int64)

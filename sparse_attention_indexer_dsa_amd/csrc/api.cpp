@@ -1,0 +1,233 @@
+// C ABI of the indexer library: host-side validation, workspace sizing and dispatch.
+// Nothing here allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa_index.h"
+#include "launch.h"
+
+namespace dsa {
+size_t topk_lds_bytes(int max_cand, int p2);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status_t device_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_precision(int p) { return p == DSA_PREC_BF16 || p == DSA_PREC_FP8 || p == DSA_PREC_MXFP8; }
+
+dsa_status_t check_precision(int p) {
+  if (!valid_precision(p))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "unsupported DSA indexer scoring precision %d; expected bf16 (0), fp8 (1) or mxfp8 (2)", p);
+  return DSA_OK;
+}
+
+dsa_status_t check_hd(int H, int D, bool need_h) {
+  if (D <= 0 || (need_h && H <= 0)) return fail(DSA_ERR_INVALID_ARGUMENT, "H and D must be positive (H=%d, D=%d)", H, D);
+  if (need_h && H != 16 && H != 32 && H != 64)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer heads H=%d unsupported; expected 16, 32 or 64", H);
+  if (D != 64 && D != 128) return fail(DSA_ERR_UNSUPPORTED, "head dim D=%d unsupported; expected 64 or 128", D);
+  return DSA_OK;
+}
+
+int max_candidates(int max_seqlen, int kpool) { return kpool == 1 ? max_seqlen : max_seqlen / kpool; }
+
+int row_stride(int max_cand) {
+  const int c = max_cand < 1 ? 1 : max_cand;
+  return (c + 63) / 64 * 64;
+}
+
+int topk_p2(int topk, int max_cand) {
+  int p2 = 1;
+  while (p2 < topk && p2 < max_cand) p2 <<= 1;
+  return p2;
+}
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status_t dsa_index_preprocess(
+    const void* q_in, const void* k_in, dsa_dtype_t in_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs,
+    const float* ln_gamma, const float* ln_beta, float ln_eps,
+    const float* rope_cos, const float* rope_sin,
+    int32_t rope_dim, int32_t rope_max_pos, int32_t rope_interleaved,
+    int32_t rope_fp32, dsa_precision_t precision,
+    void* q_op, uint8_t* q_scale, void* k_op, uint8_t* k_scale,
+    float* q_f32_out, float* k_f32_out,
+    hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_precision((int)precision)) != DSA_OK) return st;
+  if (in_dtype != DSA_DTYPE_BF16 && in_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "in_dtype %d must be bf16 (0) or fp32 (1)", (int)in_dtype);
+  if (!q_in && !k_in) return fail(DSA_ERR_INVALID_ARGUMENT, "q_in and k_in are both NULL");
+  if (T < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "T=%d and S=%d must be non-negative", T, S);
+  if (q_in && k_in && T != S) return fail(DSA_ERR_INVALID_ARGUMENT, "T=%d != S=%d: queries and keys share cu_seqlens", T, S);
+  if ((st = check_hd(H, D, q_in != nullptr)) != DSA_OK) return st;
+  if (!cu_seqlens || num_seqs < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens must be given with num_seqs >= 1");
+  if (rope_dim < 0 || rope_dim > D || (rope_dim % 2) != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "rope_dim=%d must be even and within [0, D=%d]", rope_dim, D);
+  if (rope_dim > 0 && !rope_interleaved && rope_dim % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "rotate-half RoPE needs rope_dim %% 32 == 0 (got %d)", rope_dim);
+  if (rope_dim > 0 && (!rope_cos || !rope_sin || rope_max_pos < 1))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "rope tables and rope_max_pos >= 1 required when rope_dim > 0");
+  const bool fp8 = precision != DSA_PREC_BF16;
+  if (q_in) {
+    if (!q_op) return fail(DSA_ERR_INVALID_ARGUMENT, "q_op is NULL");
+    if (fp8 && !q_scale) return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale is NULL for an fp8 precision");
+    if (!aligned(q_in, 16) || !aligned(q_op, 16) || (q_f32_out && !aligned(q_f32_out, 16)))
+      return fail(DSA_ERR_INVALID_ARGUMENT, "query buffers must be 16-byte aligned");
+  }
+  if (k_in) {
+    if (!k_op) return fail(DSA_ERR_INVALID_ARGUMENT, "k_op is NULL");
+    if (fp8 && !k_scale) return fail(DSA_ERR_INVALID_ARGUMENT, "k_scale is NULL for an fp8 precision");
+    if (!aligned(k_in, 16) || !aligned(k_op, 16) || (k_f32_out && !aligned(k_f32_out, 16)))
+      return fail(DSA_ERR_INVALID_ARGUMENT, "key buffers must be 16-byte aligned");
+  }
+  dsa::PreprocessLaunch p;
+  p.q_in = q_in; p.k_in = k_in; p.in_bf16 = in_dtype == DSA_DTYPE_BF16;
+  p.T = q_in ? T : 0; p.S = k_in ? S : 0; p.H = H; p.D = D;
+  p.cu = cu_seqlens; p.B = num_seqs;
+  p.gamma = ln_gamma; p.beta = ln_beta; p.eps = ln_eps;
+  p.cos_t = rope_cos; p.sin_t = rope_sin;
+  p.rope_dim = rope_dim; p.max_pos = rope_max_pos; p.interleaved = rope_interleaved ? 1 : 0;
+  p.rope_fp32 = rope_fp32 ? 1 : 0; p.precision = (int)precision;
+  p.q_op = q_op; p.q_scale = q_scale; p.k_op = k_op; p.k_scale = k_scale;
+  p.q_f32 = q_f32_out; p.k_f32 = k_f32_out;
+  hipError_t e = dsa::launch_preprocess(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_preprocess");
+  return DSA_OK;
+}
+
+dsa_status_t dsa_index_kpool(
+    const void* k, dsa_dtype_t k_dtype, int32_t S, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs,
+    const uint16_t* gate_bf16, const float* slot_bias, int32_t kpool,
+    dsa_precision_t precision,
+    void* pooled_op, uint8_t* pooled_scale, int32_t* cu_pools,
+    hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_precision((int)precision)) != DSA_OK) return st;
+  if (k_dtype != DSA_DTYPE_BF16 && k_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "k_dtype %d must be bf16 (0) or fp32 (1)", (int)k_dtype);
+  if ((st = check_hd(0, D, false)) != DSA_OK) return st;
+  if (S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "S=%d must be non-negative", S);
+  if (kpool < 1 || kpool > 64) return fail(DSA_ERR_UNSUPPORTED, "kpool=%d must be within [1, 64]", kpool);
+  if (!cu_seqlens || num_seqs < 1 || !cu_pools)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens, num_seqs >= 1 and cu_pools are required");
+  if (S > 0 && (!k || !gate_bf16 || !slot_bias || !pooled_op))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "k, gate_bf16, slot_bias and pooled_op are required");
+  if (precision != DSA_PREC_BF16 && S / kpool > 0 && !pooled_scale)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "pooled_scale is NULL for an fp8 precision");
+  dsa::KpoolLaunch p;
+  p.k = k; p.k_bf16 = k_dtype == DSA_DTYPE_BF16; p.S = S; p.D = D;
+  p.cu = cu_seqlens; p.B = num_seqs;
+  p.gate = gate_bf16; p.bias = slot_bias; p.kpool = kpool;
+  p.precision = (int)precision;
+  p.pooled = pooled_op; p.pooled_scale = pooled_scale; p.cu_pools = cu_pools;
+  hipError_t e = dsa::launch_kpool(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_kpool");
+  return DSA_OK;
+}
+
+size_t dsa_index_workspace_size(int32_t T, int32_t H, int32_t D, int32_t num_seqs,
+                                int32_t max_seqlen, int32_t topk, int32_t kpool,
+                                dsa_precision_t precision) {
+  (void)H; (void)D; (void)num_seqs; (void)topk; (void)precision;
+  if (T < 0 || max_seqlen < 0 || kpool < 1) return 0;
+  const int stride = row_stride(max_candidates(max_seqlen, kpool));
+  return (size_t)T * (size_t)stride * sizeof(float) + 256;
+}
+
+dsa_status_t dsa_index_score_topk(
+    const void* q_op, const uint8_t* q_scale,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools, int32_t kpool_tail,
+    int32_t topk, float sm_scale, dsa_precision_t precision,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths,
+    int32_t* out_pool_indices,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_precision((int)precision)) != DSA_OK) return st;
+  if (w_dtype != DSA_DTYPE_BF16 && w_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "w_dtype %d must be bf16 (0) or fp32 (1)", (int)w_dtype);
+  if (T < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "T=%d and S=%d must be non-negative", T, S);
+  if ((st = check_hd(H, D, true)) != DSA_OK) return st;
+  if (topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "topk=%d must be >= 1", topk);
+  if (kpool < 1 || kpool > 64) return fail(DSA_ERR_UNSUPPORTED, "kpool=%d must be within [1, 64]", kpool);
+  if (kpool > 1 && !cu_pools) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_pools is required when kpool > 1");
+  if (!cu_seqlens || num_seqs < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens must be given with num_seqs >= 1");
+  if (max_seqlen < 0 || (T > 0 && max_seqlen < 1))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_seqlen=%d must be >= 1", max_seqlen);
+  if (T == 0) return DSA_OK;
+  const bool fp8 = precision != DSA_PREC_BF16;
+  if (!q_op || !w || !out_indices || !out_scores || !out_lengths || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (S > 0 && !k_op) return fail(DSA_ERR_INVALID_ARGUMENT, "k_op is NULL");
+  if (fp8 && (!q_scale || (S > 0 && !k_scale)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale/k_scale are required for an fp8 precision");
+  if (!aligned(q_op, 16) || (k_op && !aligned(k_op, 16)) || !aligned(workspace, 256) ||
+      !aligned(w, w_dtype == DSA_DTYPE_FP32 ? 4 : 2) || !aligned(out_indices, 4) || !aligned(out_scores, 4) ||
+      !aligned(out_lengths, 4) || (out_pool_indices && !aligned(out_pool_indices, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned buffer (operands 16 B, workspace 256 B, outputs 4 B)");
+  const int max_cand = max_candidates(max_seqlen, kpool);
+  if (max_cand > dsa::kTopkMaxCand)
+    return fail(DSA_ERR_UNSUPPORTED, "%d candidates per row exceed the supported %d", max_cand, dsa::kTopkMaxCand);
+  if (dsa::topk_lds_bytes(max_cand, topk_p2(topk, max_cand)) > kMaxLds)
+    return fail(DSA_ERR_UNSUPPORTED, "topk=%d with %d candidates per row exceeds the on-chip selection buffer",
+                topk, max_cand);
+  if ((long long)topk * kpool + kpool - 1 > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "topk*kpool overflows");
+  const size_t need = dsa_index_workspace_size(T, H, D, num_seqs, max_seqlen, topk, kpool, precision);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+
+  dsa::ScoreTopkLaunch p;
+  p.q_op = q_op; p.q_scale = q_scale; p.k_op = k_op; p.k_scale = k_scale;
+  p.w = w; p.w_bf16 = w_dtype == DSA_DTYPE_BF16;
+  p.T = T; p.S = S; p.H = H; p.D = D;
+  p.cu = cu_seqlens; p.B = num_seqs; p.max_seqlen = max_seqlen;
+  p.kpool = kpool; p.cu_pools = cu_pools; p.kpool_tail = kpool_tail ? 1 : 0;
+  p.topk = topk; p.sm_scale = sm_scale; p.precision = (int)precision;
+  p.out_indices = out_indices; p.out_scores = out_scores; p.out_lengths = out_lengths;
+  p.out_pool_indices = kpool > 1 ? out_pool_indices : nullptr;
+  p.scores = static_cast<float*>(workspace);
+  p.stride = row_stride(max_cand);
+  p.max_cand = max_cand;
+  hipError_t e = dsa::launch_score(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk (score)");
+  e = dsa::launch_topk(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk (top-k)");
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the kernels.
+// Arguments here are already validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+enum { kPrecBF16 = 0, kPrecFP8 = 1, kPrecMXFP8 = 2 };
+
+struct PreprocessLaunch {
+  const void* q_in; const void* k_in; bool in_bf16;
+  int T, S, H, D;
+  const int32_t* cu; int B;
+  const float* gamma; const float* beta; float eps;
+  const float* cos_t; const float* sin_t;
+  int rope_dim, max_pos, interleaved, rope_fp32;
+  int precision;
+  void* q_op; uint8_t* q_scale; void* k_op; uint8_t* k_scale;
+  float* q_f32; float* k_f32;
+};
+hipError_t launch_preprocess(const PreprocessLaunch& p, hipStream_t st);
+
+struct KpoolLaunch {
+  const void* k; bool k_bf16; int S, D;
+  const int32_t* cu; int B;
+  const uint16_t* gate; const float* bias; int kpool;
+  int precision;
+  void* pooled; uint8_t* pooled_scale; int32_t* cu_pools;
+};
+hipError_t launch_kpool(const KpoolLaunch& p, hipStream_t st);
+
+struct ScoreTopkLaunch {
+  const void* q_op; const uint8_t* q_scale;
+  const void* k_op; const uint8_t* k_scale;
+  const void* w; bool w_bf16;
+  int T, S, H, D;
+  const int32_t* cu; int B; int max_seqlen;
+  int kpool; const int32_t* cu_pools; int kpool_tail;
+  int topk; float sm_scale; int precision;
+  int32_t* out_indices; float* out_scores; int32_t* out_lengths; int32_t* out_pool_indices;
+  float* scores;          // workspace: [T, stride] fp32
+  int stride;             // row stride of the score workspace (floats)
+  int max_cand;           // candidates per row upper bound
+};
+hipError_t launch_score(const ScoreTopkLaunch& p, hipStream_t st);
+hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st);
+
+// Largest row (candidates) the LDS top-k supports.
+constexpr int kTopkMaxCand = 32768;
+
+}  // namespace dsa

@@ -1,0 +1,340 @@
+// Fused indexer preprocessing and quantisation (gfx950).
+//
+// Keys: LayerNorm over D (pinned pairwise halving sums), then RoPE, then quantisation.
+// Queries: RoPE, then quantisation. Everything runs in fp32 with one rounding per
+// operation (this file is built without floating-point contraction); with rope_fp32 off
+// the input and the output of RoPE are rounded to bf16 (the default path's materialised
+// BF16, Megatron-LM PR 8403, "What does this PR do?" and "Motivation").
+//
+// Layouts. Queries: one vector (t,h) of D elements per group of D/8 lanes, lane g holding
+// the 8 contiguous elements 8g..8g+7 (16-byte loads and stores). Keys: one token per
+// group of 16 lanes, lane g holding elements g, g+16, g+32, ... so that the halving sum
+// a[i] += a[i+n] is in-lane for n >= 16 and a single shuffle for n = 8, 4, 2, 1.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+struct PreArgs {
+  const void* q_in; const void* k_in;
+  int T, S, H, D;
+  const int32_t* cu; int B;
+  const float* gamma; const float* beta; float eps;
+  const float* cos_t; const float* sin_t;
+  int R, max_pos, interleaved, rope_fp32;
+  void* q_op; uint8_t* q_scale; void* k_op; uint8_t* k_scale;
+  float* q_f32; float* k_f32;
+};
+
+__device__ __forceinline__ int token_position(const int32_t* cu, int B, int T, int t) {
+  int b = find_doc(cu, B, t);
+  int start = clampi(__ldg(cu + b), 0, T);
+  return max(0, t - start);
+}
+
+// ------------------------------------------------------------------ queries
+
+template <int D, bool IN_BF16, int PREC>
+__global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
+  constexpr int G = D / 8;                       // lanes per vector
+  constexpr int VPB = 256 / G;                   // vectors per block
+  const int g = threadIdx.x % G;
+  const long long v = (long long)blockIdx.x * VPB + threadIdx.x / G;
+  const long long nvec = (long long)a.T * a.H;
+  const bool live = v < nvec;
+  const long long vv = live ? v : 0;
+  const int t = (int)(vv / a.H);
+
+  float x[8];
+  if (IN_BF16) {
+    uint4 raw = live ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q_in) + vv * D + 8 * g)
+                     : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = u2f(w[j] << 16);
+      x[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q_in) + vv * D + 8 * g);
+    float4 lo = live ? p[0] : make_float4(0, 0, 0, 0), hi = live ? p[1] : make_float4(0, 0, 0, 0);
+    x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w; x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+  }
+  if (!a.rope_fp32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = bf16_round(x[j]);
+  }
+
+  if (a.R > 0) {
+    const int rs = D - a.R;
+    const int pos = min(token_position(a.cu, a.B, a.T, t), a.max_pos - 1);
+    const int half = a.R / 2;
+    const float* crow = a.cos_t + (long long)pos * half;
+    const float* srow = a.sin_t + (long long)pos * half;
+    if (a.interleaved) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int e = 8 * g + j;
+        if (e >= rs) {
+          const int col = (e - rs) / 2;
+          const float c = crow[col], s = srow[col];
+          const float x1 = x[j], x2 = x[j + 1];
+          x[j] = x1 * c - x2 * s;
+          x[j + 1] = x2 * c + x1 * s;
+        }
+      }
+    } else {
+      // partner lane holds the other half of each rotated pair in the same slot
+      const int lanes_half = half / 8;
+      const bool in_rope = 8 * g >= rs;
+      const bool first = 8 * g < rs + half;
+      const int src_g = !in_rope ? g : (first ? g + lanes_half : g - lanes_half);
+      const int src = (threadIdx.x & 63) - g + src_g;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = __shfl(x[j], src, 64);
+      if (in_rope) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = 8 * g + j - rs - (first ? 0 : half);
+          const float c = crow[col], s = srow[col];
+          x[j] = first ? (x[j] * c - p[j] * s) : (x[j] * c + p[j] * s);
+        }
+      }
+    }
+    if (!a.rope_fp32) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = bf16_round(x[j]);
+    }
+  }
+
+  if (a.q_f32 && live) {
+    float4* o = reinterpret_cast<float4*>(a.q_f32 + vv * D + 8 * g);
+    o[0] = make_float4(x[0], x[1], x[2], x[3]);
+    o[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+
+  if (PREC == kPrecBF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)f32_to_bf16_rne(x[2 * j]) | ((uint32_t)f32_to_bf16_rne(x[2 * j + 1]) << 16);
+    if (live)
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op) + vv * D + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    // per-vector: reduce over the G lanes; per-32: over 4 lanes
+    constexpr int RED = (PREC == kPrecFP8) ? G : 4;
+#pragma unroll
+    for (int off = 1; off < RED; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const int e = ue8m0_exponent(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= e4m3_encode(ldexpf(x[j], -e)) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= e4m3_encode(ldexpf(x[4 + j], -e)) << (8 * j);
+    if (live) {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.q_op) + vv * D + 8 * g) = make_uint2(lo, hi);
+      if (PREC == kPrecFP8) {
+        if (g == 0) a.q_scale[vv] = (uint8_t)(e + 127);
+      } else {
+        if ((g & 3) == 0) a.q_scale[vv * (D / 32) + g / 4] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ keys
+
+template <int D, bool IN_BF16, int PREC>
+__global__ __launch_bounds__(256) void preprocess_k_kernel(PreArgs a) {
+  constexpr int V = D / 16;                      // elements per lane
+  const int g = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63;
+  const int gbase = lane - g;
+  const int s_raw = blockIdx.x * 16 + threadIdx.x / 16;
+  const bool live = s_raw < a.S;
+  const int s = live ? s_raw : 0;
+
+  float x[V];
+#pragma unroll
+  for (int m = 0; m < V; ++m) {
+    const long long off = (long long)s * D + g + 16 * m;
+    x[m] = IN_BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k_in)[off])
+                   : reinterpret_cast<const float*>(a.k_in)[off];
+  }
+
+  if (a.gamma) {
+    // pinned halving sum: for n = D/2 .. 1: a[i] += a[i+n], i < n
+    auto tree = [&](const float* val) -> float {
+      float v[V];
+#pragma unroll
+      for (int m = 0; m < V; ++m) v[m] = val[m];
+#pragma unroll
+      for (int n = V / 2; n >= 1; n >>= 1) {
+#pragma unroll
+        for (int m = 0; m < n; ++m) v[m] = v[m] + v[m + n];
+      }
+      float r = v[0];
+#pragma unroll
+      for (int n = 8; n >= 1; n >>= 1) {
+        const float o = __shfl(r, gbase + ((g + n) & 15), 64);
+        if (g < n) r = r + o;
+      }
+      return __shfl(r, gbase, 64);
+    };
+    const float inv_d = 1.0f / (float)D;
+    const float mean = tree(x) * inv_d;
+    float d[V], dd[V];
+#pragma unroll
+    for (int m = 0; m < V; ++m) { d[m] = x[m] - mean; dd[m] = d[m] * d[m]; }
+    const float var = tree(dd) * inv_d;
+    // correctly rounded sqrt and divide (the library is built with
+    // -fhip-fp32-correctly-rounded-divide-sqrt and without denormal flushing)
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+    for (int m = 0; m < V; ++m) {
+      const int e = g + 16 * m;
+      const float y = (d[m] * rstd) * a.gamma[e];
+      x[m] = y + (a.beta ? a.beta[e] : 0.0f);
+    }
+  }
+  if (!a.rope_fp32) {
+#pragma unroll
+    for (int m = 0; m < V; ++m) x[m] = bf16_round(x[m]);
+  }
+
+  if (a.R > 0) {
+    const int rs = D - a.R;
+    const int pos = min(token_position(a.cu, a.B, a.S, s), a.max_pos - 1);
+    const int half = a.R / 2;
+    const float* crow = a.cos_t + (long long)pos * half;
+    const float* srow = a.sin_t + (long long)pos * half;
+    if (a.interleaved) {
+#pragma unroll
+      for (int m = 0; m < V; ++m) {
+        const int e = g + 16 * m;
+        const float p = __shfl_xor(x[m], 1, 64);
+        if (e >= rs) {
+          const int col = (e - rs) / 2;
+          const float c = crow[col], sn = srow[col];
+          x[m] = (e & 1) ? (x[m] * c + p * sn) : (x[m] * c - p * sn);
+        }
+      }
+    } else {
+      const int mh = half / 16;                  // partner is m +- mh, in-lane
+      float y[V];
+#pragma unroll
+      for (int m = 0; m < V; ++m) {
+        const int e = g + 16 * m;
+        y[m] = x[m];
+        if (e >= rs) {
+          const bool first = e < rs + half;
+          const int col = e - rs - (first ? 0 : half);
+          const float c = crow[col], sn = srow[col];
+          float p = 0.f;
+#pragma unroll
+          for (int mm = 0; mm < V; ++mm)
+            if (mm == (first ? m + mh : m - mh)) p = x[mm];
+          y[m] = first ? (x[m] * c - p * sn) : (x[m] * c + p * sn);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < V; ++m) x[m] = y[m];
+    }
+    if (!a.rope_fp32) {
+#pragma unroll
+      for (int m = 0; m < V; ++m) x[m] = bf16_round(x[m]);
+    }
+  }
+
+  if (a.k_f32 && live) {
+#pragma unroll
+    for (int m = 0; m < V; ++m) a.k_f32[(long long)s * D + g + 16 * m] = x[m];
+  }
+
+  if (PREC == kPrecBF16) {
+    if (live) {
+#pragma unroll
+      for (int m = 0; m < V; ++m)
+        reinterpret_cast<uint16_t*>(a.k_op)[(long long)s * D + g + 16 * m] = f32_to_bf16_rne(x[m]);
+    }
+  } else if (PREC == kPrecFP8) {
+    float amax = 0.f;
+#pragma unroll
+    for (int m = 0; m < V; ++m) amax = fmaxf(amax, fabsf(x[m]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const int e = ue8m0_exponent(amax);
+    if (live) {
+#pragma unroll
+      for (int m = 0; m < V; ++m)
+        reinterpret_cast<uint8_t*>(a.k_op)[(long long)s * D + g + 16 * m] = (uint8_t)e4m3_encode(ldexpf(x[m], -e));
+      if (g == 0) a.k_scale[s] = (uint8_t)(e + 127);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < V / 2; ++b) {            // 32-element block b = slots m = 2b, 2b+1
+      float amax = fmaxf(fabsf(x[2 * b]), fabsf(x[2 * b + 1]));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      const int e = ue8m0_exponent(amax);
+      if (live) {
+        uint8_t* o = reinterpret_cast<uint8_t*>(a.k_op) + (long long)s * D;
+        o[g + 32 * b] = (uint8_t)e4m3_encode(ldexpf(x[2 * b], -e));
+        o[g + 32 * b + 16] = (uint8_t)e4m3_encode(ldexpf(x[2 * b + 1], -e));
+        if (g == 0) a.k_scale[(long long)s * (D / 32) + b] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
+template <int D, bool IN_BF16, int PREC>
+hipError_t launch_pre(const PreArgs& a, hipStream_t st) {
+  if (a.q_in && a.T > 0) {
+    const long long nvec = (long long)a.T * a.H;
+    const long long blocks = (nvec + (256 / (D / 8)) - 1) / (256 / (D / 8));
+    hipLaunchKernelGGL((preprocess_q_kernel<D, IN_BF16, PREC>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.k_in && a.S > 0) {
+    const int blocks = (a.S + 15) / 16;
+    hipLaunchKernelGGL((preprocess_k_kernel<D, IN_BF16, PREC>), dim3(blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D, bool IN_BF16>
+hipError_t launch_pre_p(const PreArgs& a, int prec, hipStream_t st) {
+  switch (prec) {
+    case kPrecBF16: return launch_pre<D, IN_BF16, kPrecBF16>(a, st);
+    case kPrecFP8: return launch_pre<D, IN_BF16, kPrecFP8>(a, st);
+    default: return launch_pre<D, IN_BF16, kPrecMXFP8>(a, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const PreprocessLaunch& p, hipStream_t st) {
+  PreArgs a;
+  a.q_in = p.q_in; a.k_in = p.k_in;
+  a.T = p.T; a.S = p.S; a.H = p.H; a.D = p.D;
+  a.cu = p.cu; a.B = p.B;
+  a.gamma = p.gamma; a.beta = p.beta; a.eps = p.eps;
+  a.cos_t = p.cos_t; a.sin_t = p.sin_t;
+  a.R = p.rope_dim; a.max_pos = p.max_pos; a.interleaved = p.interleaved; a.rope_fp32 = p.rope_fp32;
+  a.q_op = p.q_op; a.q_scale = p.q_scale; a.k_op = p.k_op; a.k_scale = p.k_scale;
+  a.q_f32 = p.q_f32; a.k_f32 = p.k_f32;
+  if (p.D == 128) return p.in_bf16 ? launch_pre_p<128, true>(a, p.precision, st) : launch_pre_p<128, false>(a, p.precision, st);
+  return p.in_bf16 ? launch_pre_p<64, true>(a, p.precision, st) : launch_pre_p<64, false>(a, p.precision, st);
+}
+
+}  // namespace dsa

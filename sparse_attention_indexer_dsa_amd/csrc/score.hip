@@ -1,0 +1,297 @@
+// Indexer scoring on gfx950 matrix cores.
+//
+// For query t and candidate c (a key, or a pooled key when kpool > 1):
+//     I[t,c] = sm_scale * sum_h w[t,h] * ReLU(q[t,h,:] . k[c,:])
+// (Megatron-LM PR 8403: per-head weights passed to the scoring call, codex review
+// finding 3; ReLU scoring, finding 1.) The q.k contraction over D runs on MFMA with fp32
+// accumulation; ReLU, the weights, the head sum and the causal mask are applied to the
+// MFMA result in registers, so per-head logits never leave the chip. Only the per-query
+// scores of causal candidates are written, to the score workspace (row stride fixed).
+//
+// Work decomposition. A workgroup of 4 waves owns 256/H consecutive query tokens of one
+// document; each wave owns 64 MFMA rows = 64/H tokens x H heads, whose q operands stay in
+// registers for the whole sweep. The workgroup sweeps the document's causal keys in LDS
+// tiles of 64 keys (two 32-key MFMA column blocks). Workgroups are numbered from the end
+// of the documents so the longest causal rows start first.
+//
+// MFMA shapes (lane l, h = l/32):
+//   bf16  v_mfma_f32_32x32x16_bf16: A lane holds row l%32, k = 8h .. 8h+7.
+//   fp8   v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3): A lane holds row l%32,
+//         bytes 0-15 = k 16h..16h+15, bytes 16-31 = k 32+16h..32+16h+15; the scale of
+//         32-element block j of row m is supplied by lane m + 32j. B mirrors A.
+//   C (32x32 fp32): lane l holds column l%32, rows 8(i/4) + 4h + (i%4), i = 0..15.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kNK = 64;          // keys per LDS tile
+constexpr int kThreads = 256;
+
+struct ScoreArgs {
+  const void* q_op; const uint8_t* q_scale;
+  const void* k_op; const uint8_t* k_scale;
+  const void* w;
+  int T, S, B, max_seqlen, kpool;
+  const int32_t* cu; const int32_t* cu_pools;
+  float sm_scale;
+  float* scores; int stride; int max_cand;
+  int ntiles;                    // query tiles per document (ceil(max_seqlen / tokens per workgroup))
+};
+
+__device__ __forceinline__ float pair_sum(float x) {
+  // lanes l and l^32 hold the two halves of the rows of one column: add them
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return u2f(r[0]) + u2f(r[1]);
+}
+
+template <int H, int D, int PREC, bool W_BF16>
+__global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
+  constexpr bool kFP8 = PREC != kPrecBF16;
+  constexpr int ES = kFP8 ? 1 : 2;               // operand bytes per element
+  constexpr int RB = D * ES;                     // operand bytes per key row
+  constexpr int ROWB = RB + 16;                  // padded LDS row
+  constexpr int KSTEPS = kFP8 ? D / 64 : D / 16; // MFMAs per 32x32 output block
+  constexpr int TPW = 64 / H;                    // tokens per wave
+  constexpr int TQ = 4 * TPW;                    // tokens per workgroup
+  constexpr int NSB = D / 32;                    // 32-element scale blocks per row
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kNK * ROWB];
+  __shared__ uint8_t ks_lds[kFP8 ? kNK * NSB : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+
+  // ---- which document and query tile
+  const int b = blockIdx.x % a.B;
+  const int p = a.ntiles - 1 - blockIdx.x / a.B;
+  const int lo = clampi(a.cu[b], 0, a.T);
+  const int hi = clampi(a.cu[b + 1], lo, a.T);
+  const int L = min(hi - lo, a.max_seqlen);
+  const int u0 = p * TQ;
+  if (u0 >= L) return;
+  const int kp = a.kpool;
+  const int u_last = min(u0 + TQ, L) - 1;
+  const int n_keys = min((u_last + 1) / kp, a.max_cand);
+  const int kbase = kp == 1 ? lo : a.cu_pools[b];
+
+  // ---- q operands, scales and weights of this wave's 64 rows (resident)
+  const int ut0 = u0 + wv * TPW;                 // first token position of the wave
+  typedef typename std::conditional<kFP8, i32x8, bf16x8>::type AType;
+  AType aop[2][KSTEPS];
+  int asc[2][KSTEPS];
+  float wl[2][16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = rb * 32 + col;                 // operand row held by this lane
+    const int tl = r / H, h = r % H;
+    const bool ok = ut0 + tl < L;
+    const long long vec = (long long)(lo + ut0 + tl) * H + h;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kFP8) {
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.q_op) + vec * D + kk * 64 + 16 * hl;
+        uint4 v0 = ok ? *reinterpret_cast<const uint4*>(base) : make_uint4(0, 0, 0, 0);
+        uint4 v1 = ok ? *reinterpret_cast<const uint4*>(base + 32) : make_uint4(0, 0, 0, 0);
+        i32x8 t8;
+        t8[0] = v0.x; t8[1] = v0.y; t8[2] = v0.z; t8[3] = v0.w;
+        t8[4] = v1.x; t8[5] = v1.y; t8[6] = v1.z; t8[7] = v1.w;
+        aop[rb][kk] = *reinterpret_cast<AType*>(&t8);
+        int s = 127;
+        if (ok) s = PREC == kPrecFP8 ? a.q_scale[vec] : a.q_scale[vec * NSB + 2 * kk + hl];
+        asc[rb][kk] = s;
+      } else {
+        const uint16_t* base = reinterpret_cast<const uint16_t*>(a.q_op) + vec * D + kk * 16 + 8 * hl;
+        uint4 v = ok ? *reinterpret_cast<const uint4*>(base) : make_uint4(0, 0, 0, 0);
+        aop[rb][kk] = *reinterpret_cast<AType*>(&v);
+        asc[rb][kk] = 0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = rb * 32 + (i / 4) * 8 + hl * 4 + (i % 4);
+      const int tl2 = rr / H, h2 = rr % H;
+      float wv_ = 0.f;
+      if (ut0 + tl2 < L) {
+        const long long wi = (long long)(lo + ut0 + tl2) * H + h2;
+        wv_ = W_BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.w)[wi]) : reinterpret_cast<const float*>(a.w)[wi];
+      }
+      wl[rb][i] = wv_;
+    }
+  }
+
+  // candidates of the tokens this lane writes (see the epilogue)
+  int cand_tok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int u = ut0 + j;
+    cand_tok[j] = (j < TPW && u < L) ? min((u + 1) / kp, a.max_cand) : 0;
+  }
+
+  const int n_tiles = (n_keys + kNK - 1) / kNK;
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int c0 = kt * kNK;
+    __syncthreads();
+    // ---- stage the key tile (zero rows past the candidates or the key array)
+    constexpr int CH = RB / 16;                  // 16-byte chunks per key row
+#pragma unroll
+    for (int it = 0; it < (kNK * CH + kThreads - 1) / kThreads; ++it) {
+      const int ch = it * kThreads + tid;
+      if (ch < kNK * CH) {
+        const int row = ch / CH, cc = ch % CH;
+        const int c = c0 + row;
+        const long long krow = (long long)kbase + c;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < n_keys && krow < a.S)
+          v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.k_op) + krow * RB + cc * 16);
+        *reinterpret_cast<uint4*>(k_lds + row * ROWB + cc * 16) = v;
+      }
+    }
+    if (kFP8) {
+      for (int i = tid; i < kNK * NSB; i += kThreads) {
+        const int row = i / NSB, blk = i % NSB;
+        const int c = c0 + row;
+        const long long krow = (long long)kbase + c;
+        uint8_t s = 127;
+        if (c < n_keys && krow < a.S) s = PREC == kPrecFP8 ? a.k_scale[krow] : a.k_scale[krow * NSB + blk];
+        ks_lds[i] = s;
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int krow_l = nb * 32 + col;          // key (LDS row) of this lane's B operand / C column
+      f32x16 acc[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        if (kFP8) {
+          const uint8_t* src = k_lds + krow_l * ROWB + kk * 64 + 16 * hl;
+          uint4 v0 = *reinterpret_cast<const uint4*>(src);
+          uint4 v1 = *reinterpret_cast<const uint4*>(src + 32);
+          i32x8 bop;
+          bop[0] = v0.x; bop[1] = v0.y; bop[2] = v0.z; bop[3] = v0.w;
+          bop[4] = v1.x; bop[5] = v1.y; bop[6] = v1.z; bop[7] = v1.w;
+          const int bsc = ks_lds[krow_l * NSB + 2 * kk + hl];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                *reinterpret_cast<const i32x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0, asc[rb][kk], 0, bsc);
+        } else {
+          uint4 v = *reinterpret_cast<const uint4*>(k_lds + krow_l * ROWB + kk * 32 + 16 * hl);
+          bf16x8 bop = *reinterpret_cast<bf16x8*>(&v);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0);
+        }
+      }
+
+      // ---- ReLU, weights and head sum in registers
+      const int c = c0 + nb * 32 + col;          // candidate index (document-local)
+      if (H == 64) {
+        float s = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), s);
+        s = pair_sum(s) * a.sm_scale;
+        if (hl == 0 && c < cand_tok[0])
+          a.scores[(long long)(lo + ut0) * a.stride + c] = s;
+      } else if (H == 32) {
+        float s[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), v);
+          s[rb] = pair_sum(v) * a.sm_scale;
+        }
+        // lanes 0-31 write token 0, lanes 32-63 token 1
+        const int ct = hl ? cand_tok[1] : cand_tok[0];
+        if (c < ct) a.scores[(long long)(lo + ut0 + hl) * a.stride + c] = hl ? s[1] : s[0];
+      } else {                                   // H == 16: rows 0-15 / 16-31 of a block are two tokens
+        float s[4];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v0 = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), v0);
+#pragma unroll
+          for (int i = 8; i < 16; ++i) v1 = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), v1);
+          s[2 * rb] = pair_sum(v0) * a.sm_scale;
+          s[2 * rb + 1] = pair_sum(v1) * a.sm_scale;
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int j = 2 * rb + hl;
+          const float v = hl ? s[2 * rb + 1] : s[2 * rb];
+          const int ct = hl ? cand_tok[2 * rb + 1] : cand_tok[2 * rb];
+          if (c < ct) a.scores[(long long)(lo + ut0 + j) * a.stride + c] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int H, int D, int PREC>
+hipError_t launch_h(const ScoreArgs& a, bool w_bf16, hipStream_t st) {
+  const long long blocks = (long long)a.ntiles * a.B;
+  if (blocks == 0) return hipSuccess;
+  if (w_bf16)
+    hipLaunchKernelGGL((score_kernel<H, D, PREC, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((score_kernel<H, D, PREC, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int PREC>
+hipError_t launch_d(const ScoreArgs& a, int H, bool w_bf16, hipStream_t st) {
+  switch (H) {
+    case 16: return launch_h<16, D, PREC>(a, w_bf16, st);
+    case 32: return launch_h<32, D, PREC>(a, w_bf16, st);
+    default: return launch_h<64, D, PREC>(a, w_bf16, st);
+  }
+}
+
+template <int PREC>
+hipError_t launch_p(const ScoreArgs& a, int H, int D, bool w_bf16, hipStream_t st) {
+  return D == 128 ? launch_d<128, PREC>(a, H, w_bf16, st) : launch_d<64, PREC>(a, H, w_bf16, st);
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreTopkLaunch& p, hipStream_t st) {
+  ScoreArgs a;
+  a.q_op = p.q_op; a.q_scale = p.q_scale; a.k_op = p.k_op; a.k_scale = p.k_scale;
+  a.w = p.w;
+  a.T = p.T; a.S = p.S; a.B = p.B; a.max_seqlen = p.max_seqlen; a.kpool = p.kpool;
+  a.cu = p.cu; a.cu_pools = p.cu_pools;
+  a.sm_scale = p.sm_scale;
+  a.scores = p.scores; a.stride = p.stride; a.max_cand = p.max_cand;
+  const int tq = 256 / p.H;
+  a.ntiles = (p.max_seqlen + tq - 1) / tq;
+  switch (p.precision) {
+    case kPrecBF16: return launch_p<kPrecBF16>(a, p.H, p.D, p.w_bf16, st);
+    case kPrecFP8: return launch_p<kPrecFP8>(a, p.H, p.D, p.w_bf16, st);
+    default: return launch_p<kPrecMXFP8>(a, p.H, p.D, p.w_bf16, st);
+  }
+}
+
+}  // namespace dsa

@@ -1,0 +1,113 @@
+"""The C ABI library on the CPU: it loads, exports every function include/dsa_index.h
+declares, sizes workspaces on the host, and rejects invalid or unsupported arguments with
+the documented status codes before touching any device (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_index.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_attention_indexer_dsa_amd as dsa
+    return dsa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
+    assert {"dsa_index_preprocess", "dsa_index_kpool", "dsa_index_workspace_size", "dsa_index_score_topk",
+            "dsa_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_size(lib):
+    ws = lib.dsa_index_workspace_size
+    # fp32 scores at a row stride rounded up to 64 candidates, plus 256 bytes
+    assert ws(8192, 64, 128, 2, 4096, 512, 1, 1) == 8192 * 4096 * 4 + 256
+    assert ws(32768, 64, 128, 12, 6144, 2048, 1, 2) == 32768 * 6144 * 4 + 256
+    assert ws(65536, 64, 128, 1, 65536, 2048, 4, 0) == 65536 * 16384 * 4 + 256
+    assert ws(10, 16, 64, 1, 100, 8, 1, 0) == 10 * 128 * 4 + 256
+    assert ws(-1, 16, 64, 1, 100, 8, 1, 0) == 0
+
+
+FAKE = 1 << 20          # an aligned host integer that is never dereferenced: validation fails first
+
+
+def _score(lib, **kw):
+    a = dict(q_op=FAKE, q_scale=FAKE, k_op=FAKE, k_scale=FAKE, w=FAKE, w_dtype=1, T=64, S=64, H=64, D=128,
+             cu=FAKE, B=1, max_seqlen=64, kpool=1, cu_pools=None, tail=1, topk=8, sm=1.0, prec=0,
+             oi=FAKE, os=FAKE, ol=FAKE, op=None, ws=FAKE, wsb=10, stream=None)
+    a.update(kw)
+    return lib.dsa_index_score_topk(a["q_op"], a["q_scale"], a["k_op"], a["k_scale"], a["w"], a["w_dtype"],
+                                    a["T"], a["S"], a["H"], a["D"], a["cu"], a["B"], a["max_seqlen"], a["kpool"],
+                                    a["cu_pools"], a["tail"], a["topk"], a["sm"], a["prec"], a["oi"], a["os"],
+                                    a["ol"], a["op"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_score_topk_validation(lib):
+    assert _score(lib, prec=7) == 2
+    assert b"unsupported DSA indexer scoring precision 7" in lib.dsa_last_error()
+    assert _score(lib, H=48) == 2
+    assert _score(lib, D=96) == 2
+    assert _score(lib, topk=0) == 1
+    assert _score(lib, cu=None) == 1
+    assert _score(lib, kpool=4, cu_pools=None) == 1
+    assert _score(lib, kpool=65) == 2
+    assert _score(lib, w_dtype=5) == 1
+    assert _score(lib, prec=1, q_scale=None) == 1
+    assert _score(lib, q_op=FAKE + 8) == 1                  # misaligned operand
+    assert _score(lib, max_seqlen=1 << 17) == 2             # more candidates than the LDS selection holds
+    assert _score(lib, topk=4096, max_seqlen=32768) == 2
+    assert _score(lib, wsb=10) == 3                         # everything valid but the workspace
+    assert b"workspace" in lib.dsa_last_error()
+    assert _score(lib, T=0) == 0                            # empty problem: nothing to do
+
+
+def _pre(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, dt=0, T=64, S=64, H=64, D=128, cu=FAKE, B=1, g=None, b=None, eps=1e-6, cos=None,
+             sin=None, R=0, maxpos=0, inter=0, f32=0, prec=0, qo=FAKE, qs=FAKE, ko=FAKE, ks=FAKE, qf=None, kf=None)
+    a.update(kw)
+    return lib.dsa_index_preprocess(a["q"], a["k"], a["dt"], a["T"], a["S"], a["H"], a["D"], a["cu"], a["B"],
+                                    a["g"], a["b"], a["eps"], a["cos"], a["sin"], a["R"], a["maxpos"], a["inter"],
+                                    a["f32"], a["prec"], a["qo"], a["qs"], a["ko"], a["ks"], a["qf"], a["kf"], None)
+
+
+def test_preprocess_validation(lib):
+    assert _pre(lib, prec=3) == 2
+    assert b"expected bf16" in lib.dsa_last_error()
+    assert _pre(lib, q=None, k=None) == 1
+    assert _pre(lib, S=65) == 1                             # queries and keys share cu_seqlens
+    assert _pre(lib, R=63, cos=FAKE, sin=FAKE, maxpos=10) == 2
+    assert _pre(lib, R=48, cos=FAKE, sin=FAKE, maxpos=10) == 2   # rotate-half needs a multiple of 32
+    assert _pre(lib, R=64, cos=None, sin=None, maxpos=10) == 1
+    assert _pre(lib, R=130, cos=FAKE, sin=FAKE, maxpos=10, inter=1) == 2
+    assert _pre(lib, prec=1, qs=None) == 1
+    assert _pre(lib, dt=9) == 1
+    assert _pre(lib, H=8) == 2
+    assert _pre(lib, cu=None) == 1
+
+
+def test_kpool_validation(lib):
+    f = lib.dsa_index_kpool
+    assert f(FAKE, 0, 64, 128, FAKE, 1, FAKE, FAKE, 0, 0, FAKE, None, FAKE, None) == 2
+    assert f(FAKE, 0, 64, 128, FAKE, 1, FAKE, FAKE, 4, 9, FAKE, None, FAKE, None) == 2
+    assert f(FAKE, 0, 64, 100, FAKE, 1, FAKE, FAKE, 4, 0, FAKE, None, FAKE, None) == 2
+    assert f(FAKE, 0, 64, 128, None, 1, FAKE, FAKE, 4, 0, FAKE, None, FAKE, None) == 1
+    assert f(FAKE, 0, 64, 128, FAKE, 1, FAKE, FAKE, 4, 1, FAKE, None, FAKE, None) == 1   # fp8 needs scales
+
+
+def test_python_binding_maps_errors():
+    import sparse_attention_indexer_dsa_amd as dsa
+    with pytest.raises(ValueError, match="unsupported DSA indexer scoring precision"):
+        dsa._prec("fp4")
+    with pytest.raises(ValueError):
+        dsa._check(2, "x")
+    with pytest.raises(RuntimeError):
+        dsa._check(3, "x")
