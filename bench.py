@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA lightning-indexer hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already resident in HBM:
+preprocess + quantise (when the workload has it), KPool compression (when it has it),
+scoring and top-k selection (with pool expansion). The metric is indexer query-key pairs
+scored and top-k'd per second: pairs = sum over queries of their causal candidates (keys,
+or pools for KPool). The default workload is 2 x 4096 tokens, 64 heads, head dim 128,
+key LayerNorm + RoPE (64 dims) in fp32, FP8 E4M3 with per-vector UE8M0 scales, topk 512.
+
+Prints ONE JSON line. Per-kernel times come from HIP events recorded on the stream the
+kernels run on, around each library call, averaged over the timed steps. The roofline
+entry is for the scoring kernel (MFMA-bound): algorithmic flops 2*H*D per pair.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_FLOPS = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp8": 5.0e15}    # MI355X dense MFMA
+PEAK_HBM = 8.0e12                                                  # MI355X HBM3E bytes/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("score.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "sparse_attention_indexer_dsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pair_count(cu, kp):
+    L = np.diff(np.asarray(cu, np.int64))
+    if kp == 1:
+        return int(np.sum(L * (L + 1) // 2))
+    tot = 0
+    for n in L:
+        u = np.arange(n)
+        tot += int(np.sum((u + 1) // kp))
+    return tot
+
+
+def run_gpu(inp, steps, warmup):
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    import parity
+    dsa.load()
+    dev = "cuda"
+    T, H, D = inp["q"].shape
+    prec, kp, topk, max_seqlen = inp["precision"], inp["kpool"], inp["topk"], inp["max_seqlen"]
+    B = len(inp["docs"])
+    d = parity.gpu_inputs(inp)
+    esz = 2 if prec == "bf16" else 1
+    nsb = {"bf16": 0, "fp8": 1, "mxfp8": D // 32}[prec]
+    odt = torch.bfloat16 if prec == "bf16" else torch.uint8
+    ops = {}
+    if inp["preprocess"]:
+        ops["q_op"] = torch.empty((T, H, D), dtype=odt, device=dev)
+        ops["k_op"] = torch.empty((T, D), dtype=odt, device=dev)
+        if prec != "bf16":
+            ops["q_scale"] = torch.empty((T, H) if prec == "fp8" else (T, H, nsb), dtype=torch.uint8, device=dev)
+            ops["k_scale"] = torch.empty((T,) if prec == "fp8" else (T, nsb), dtype=torch.uint8, device=dev)
+        q_op, k_src = ops["q_op"], ops["k_op"]
+    else:
+        q_op, k_src = d["q"], d["k"]
+    pool = {}
+    if kp > 1:
+        P = T // kp
+        pool["pooled_op"] = torch.empty((P, D), dtype=odt, device=dev)
+        pool["cu_pools"] = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        if prec != "bf16":
+            pool["pooled_scale"] = torch.empty((P,) if prec == "fp8" else (P, nsb), dtype=torch.uint8, device=dev)
+    ws = torch.empty(dsa.workspace_size(T, max_seqlen, topk, kp, H, D, B, prec), dtype=torch.uint8, device=dev)
+    outs = dsa._alloc_outputs(None, T, topk, kp, dev)
+    k_op = pool["pooled_op"] if kp > 1 else (ops["k_op"] if inp["preprocess"] else d["k"])
+    k_scale = pool.get("pooled_scale") if kp > 1 else ops.get("k_scale")
+
+    def step(ev=None):
+        i = 0
+        if ev is not None:
+            ev[i].record(); i += 1
+        if inp["preprocess"]:
+            dsa.preprocess(d["q"], d["k"], d["cu"], ln_gamma=d.get("gamma") if inp["layernorm"] else None,
+                           ln_beta=d.get("beta") if inp["layernorm"] else None, ln_eps=1e-6,
+                           rope_cos=d.get("cos"), rope_sin=d.get("sin"), rope_dim=inp["rope_dim"],
+                           rope_fp32=inp["rope_fp32"], precision=prec, out=ops)
+        if ev is not None:
+            ev[i].record(); i += 1
+        if kp > 1:
+            dsa.kpool(k_src, d["cu"], d["gate"], d["bias"], kp, precision=prec, out=pool)
+        if ev is not None:
+            ev[i].record(); i += 1
+        dsa.score(q_op, k_op, d["w"], d["cu"], max_seqlen, ws, q_scale=ops.get("q_scale"), k_scale=k_scale,
+                  precision=prec, kpool=kp, cu_pools=pool.get("cu_pools"))
+        if ev is not None:
+            ev[i].record(); i += 1
+        dsa.topk(ws, T, d["cu"], max_seqlen, topk, kpool=kp, cu_pools=pool.get("cu_pools"), kpool_tail=True,
+                 out=outs)
+        if ev is not None:
+            ev[i].record(); i += 1
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    names = ["preprocess", "kpool", "score", "topk"]
+    per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])) / 1e3
+           for i, n in enumerate(names)}
+    return (t1 - t0), per
+
+
+def algorithmic(inp, pairs):
+    """Algorithmic flops/bytes per launch of each kernel (measurement)."""
+    T, H, D = inp["q"].shape
+    prec, kp, topk = inp["precision"], inp["kpool"], inp["topk"]
+    esz = 2 if prec == "bf16" else 1
+    nsb = {"bf16": 0, "fp8": 1, "mxfp8": D // 32}[prec]
+    out = {"score_flops": 2.0 * H * D * pairs}
+    if inp["preprocess"]:
+        out["preprocess_bytes"] = float(T * H * D * 2 + T * H * D * esz + T * H * nsb + T * D * 2 + T * D * esz + T * nsb)
+    if kp > 1:
+        P = T // kp
+        out["kpool_bytes"] = float(T * D * 2 + T * 2 + P * D * esz)
+    width = topk if kp == 1 else topk * kp + kp - 1
+    out["topk_bytes"] = float(pairs * 4 + T * topk * 4 + T * width * 4 + T * 4 + (T * topk * 4 if kp > 1 else 0))
+    out["score_bytes"] = float(T * H * D * esz + T * H * 4 + (T // kp) * D * esz + pairs * 4)
+    return out
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle on a bounded sample of the same workload: key side in full, then query rows in
+    batches until the time budget is used; throughput extrapolated to the whole workload."""
+    from threadpoolctl import threadpool_info
+    from oracle import oracle as orc
+    import gen
+    import parity
+    cfg = parity.config_of(inp)
+    T = inp["q"].shape[0]
+    kp, topk = inp["kpool"], inp["topk"]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(T)
+    t0 = time.perf_counter()
+    o = parity.oracle_operands_rows(inp, cfg, order[:1])     # key side (LayerNorm/RoPE/quantise or KPool)
+    t_keys = time.perf_counter() - t0
+    cu = inp["cu_seqlens"]
+    _, pos = orc.geometry(cu, T)
+    done, pairs, t_rows = 0, 0, 0.0
+    batch = 16
+    while done < T and (t_rows < budget_s or done == 0):
+        rows = np.sort(order[done:done + batch])
+        t1 = time.perf_counter()
+        qo = parity.oracle_operands_rows(inp, cfg, rows, keys=False) if cfg["preprocess"] else None
+        if qo is not None:
+            q_deq = qo["q_deq"]
+        else:
+            q_deq = {int(t): orc.dequantize(inp["q"][t], None, "bf16") for t in rows}
+        orc.index_topk(q_deq, o["k_deq"], inp["w"].astype(np.float64), cu, topk, 1.0, kp, o.get("cu_pools"),
+                       True, rows=rows)
+        t_rows += time.perf_counter() - t1
+        pairs += int(np.sum((pos[rows] + 1) // kp))
+        done += rows.size
+    total_pairs = pair_count(cu, kp)
+    est = t_keys + t_rows * (total_pairs / max(pairs, 1))
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = int(blas[0]["num_threads"]) if blas else 1
+    return {"value": total_pairs / est, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "sample": (f"numpy fp64 oracle: full key side ({t_keys:.2f} s) + {done} random query rows "
+                       f"({pairs} pairs, {t_rows:.2f} s), extrapolated to all {total_pairs} pairs"),
+            "seconds": round(t_keys + t_rows, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the hot path runs on a "
+              "single MI355X; sharding across GPUs is a design note, not a measured path)", file=sys.stderr)
+        sys.exit(2)
+    import gen
+    inp = gen.workload(args.workload)
+    T, H, D = inp["q"].shape
+    kp = inp["kpool"]
+    pairs = pair_count(inp["cu_seqlens"], kp)
+    print(f"[bench] workload {args.workload}: {inp['name']} T={T} pairs={pairs}", file=sys.stderr, flush=True)
+    elapsed, per = run_gpu(inp, args.steps, args.warmup)
+    alg = algorithmic(inp, pairs)
+    prec = inp["precision"]
+    kernels = {}
+    for n in ("preprocess", "kpool", "score", "topk"):
+        if per[n] <= 0 or (n == "preprocess" and not inp["preprocess"]) or (n == "kpool" and kp == 1):
+            continue
+        k = {"ms": round(per[n] * 1e3, 4)}
+        if n == "score":
+            k["tflops"] = round(alg["score_flops"] / per[n] / 1e12, 1)
+            k["frac_mfma"] = round(alg["score_flops"] / per[n] / PEAK_FLOPS[prec], 4)
+        else:
+            b = alg[f"{n}_bytes"]
+            k["gbps"] = round(b / per[n] / 1e9, 1)
+            k["frac_hbm"] = round(b / per[n] / PEAK_HBM, 4)
+        kernels[n] = k
+    achieved = alg["score_flops"] / per["score"] / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(inp["name"])
+        if rec and rec.get("source_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+    line = {
+        "metric": "indexer query-key pairs scored+top-k'd/sec",
+        "value": pairs * args.steps / elapsed,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "mxfp8": "mxfp8-e4m3"}[prec],
+        "data": "synthetic (seeded numpy draws with the workload's shapes and distributions)",
+        "config": {"workload": inp["name"], "T": T, "H": H, "D": D, "docs": inp["docs"] if len(inp["docs"]) <= 16
+                   else f"{len(inp['docs'])} docs", "topk": inp["topk"], "kpool": kp, "precision": prec,
+                   "preprocess": bool(inp["preprocess"]), "pairs_per_step": pairs, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "score", "achieved": round(achieved, 2),
+                     "peak": PEAK_FLOPS[prec] / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / PEAK_FLOPS[prec], 4), "traffic": traffic},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,6 +161,7 @@ size_t dsa_index_workspace_size(int32_t T, int32_t H, int32_t D, int32_t num_seq
 /*
  * dsa_index_score_topk - scores of every causal candidate, then per-row top-k
  * (PR 8403 codex review findings 1-3; PR 5992 "Key changes"; PR 7522 "Changes").
+ * Equivalent to dsa_index_score followed by dsa_index_topk on the same stream.
  *
  *   q_op, q_scale  [T,H,D] scoring operands (+ scales) as produced by dsa_index_preprocess
  *   k_op, k_scale  [S,D] token keys (kpool == 1), or [S,D] pooled keys (kpool > 1, S = rows
@@ -196,6 +197,38 @@ dsa_status_t dsa_index_score_topk(
     int32_t* out_indices, float* out_scores, int32_t* out_lengths,
     int32_t* out_pool_indices,
     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_index_score - the scoring half of dsa_index_score_topk: writes the fp32 score of every
+ * causal candidate of every query row into `workspace` and nothing else. Row t occupies
+ * floats [t*stride, t*stride + cand(t)) with stride = the smallest multiple of 64 that is
+ * >= max(1, max_seqlen) (kpool == 1) or max(1, max_seqlen/kpool) (kpool > 1), and
+ * cand(t) = u+1 or floor((u+1)/kpool) for t at position u of its document; entry c is the
+ * score of document-local candidate c. Other workspace bytes are left untouched. Arguments
+ * and errors are as for dsa_index_score_topk.
+ */
+dsa_status_t dsa_index_score(
+    const void* q_op, const uint8_t* q_scale,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools,
+    float sm_scale, dsa_precision_t precision,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_index_topk - the selection half of dsa_index_score_topk: reads the score rows that
+ * dsa_index_score wrote into `workspace` (same T, cu_seqlens, max_seqlen and kpool) and
+ * writes out_indices / out_scores / out_lengths / out_pool_indices exactly as
+ * dsa_index_score_topk does.
+ */
+dsa_status_t dsa_index_topk(
+    const void* workspace, size_t workspace_bytes,
+    int32_t T, const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools, int32_t kpool_tail, int32_t topk,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths, int32_t* out_pool_indices,
+    hipStream_t stream);
 
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* dsa_last_error(void);

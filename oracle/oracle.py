@@ -152,29 +152,30 @@ def preprocess(q_in, k_in, cu_seqlens, gamma=None, beta=None, eps=1e-6,
     Positions restart at every document. With ``rope_fp32`` off every carrier
     handed from one step to the next is bf16: the input of RoPE and its output
     are rounded to bf16. With it on the carrier stays fp32 up to quantisation.
-    ``q_rows`` (optional) names the token rows ``q_in`` holds, for sampled checks.
+    ``q_rows`` (optional) names the token rows ``q_in`` holds, for sampled checks;
+    ``k_in`` may be None to skip the keys (the key carrier is then None).
     """
     q = np.asarray(q_in, dtype=F32)
-    k = np.asarray(k_in, dtype=F32)
-    S = k.shape[0]
-    T = S if q_rows is not None else q.shape[0]
-    if T != S:
-        raise ValueError("queries and keys share one cu_seqlens (T == S)")
+    T = int(np.asarray(cu_seqlens)[-1]) if q_rows is not None else q.shape[0]
     _, pos_all = geometry(cu_seqlens, T)
-    pos = pos_all
     rnd = (lambda v: v) if rope_fp32 else fm.bf16_round
 
-    y = key_layernorm(k, gamma, beta, eps) if gamma is not None else k
-    y = rnd(y)
-    if rope_dim:
-        y = rnd(rope(y, pos, cos, sin, rope_dim, interleaved))
-    k_car = y
+    k_car = None
+    if k_in is not None:
+        k = np.asarray(k_in, dtype=F32)
+        if k.shape[0] != T:
+            raise ValueError("queries and keys share one cu_seqlens (T == S)")
+        y = key_layernorm(k, gamma, beta, eps) if gamma is not None else k
+        y = rnd(y)
+        if rope_dim:
+            y = rnd(rope(y, pos_all, cos, sin, rope_dim, interleaved))
+        k_car = y.astype(F32)
 
     qpos = pos_all if q_rows is None else pos_all[np.asarray(q_rows, dtype=np.int64)]
     y = rnd(q)
     if rope_dim:
         y = rnd(rope(y, qpos[:, None], cos, sin, rope_dim, interleaved))
-    return y.astype(F32), k_car.astype(F32)
+    return y.astype(F32), k_car
 
 
 # --------------------------------------------------------------------------

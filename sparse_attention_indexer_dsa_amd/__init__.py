@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
 * ``workspace_size``   - bytes of score workspace ``score_topk`` needs.
 * ``score_topk``       - scores of all causal candidates, then the per-row top-k
                          (and pool expansion when kpool > 1).
+* ``score``, ``topk``  - the two halves of ``score_topk`` (score rows into the
+                         workspace; selection from it).
 
 Status codes 1 (invalid argument) and 2 (unsupported) raise ``ValueError``; 3 (workspace
 too small) and 4 (device error) raise ``RuntimeError``.
@@ -23,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "library_path", "load",
+__all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "topk", "library_path", "load",
            "PRECISIONS", "DsaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +65,11 @@ def load():
     lib.dsa_index_score_topk.restype = i32
     lib.dsa_index_score_topk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32, vp,
                                          i32, i32, f32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_index_score.restype = i32
+    lib.dsa_index_score.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32, vp,
+                                    f32, i32, vp, sz, vp]
+    lib.dsa_index_topk.restype = i32
+    lib.dsa_index_topk.argtypes = [vp, sz, i32, vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_last_error.argtypes = []
     _lib = lib
@@ -241,4 +248,52 @@ def score_topk(q_op, k_op, w, cu_seqlens, max_seqlen, topk, *, q_scale=None, k_s
         _ptr(out.get("pool_indices")), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(dev))
     _check(st, "dsa_index_score_topk")
+    return out
+
+
+def _alloc_outputs(out, T, topk, kpool, dev):
+    out = dict(out or {})
+    width = topk if kpool == 1 else topk * kpool + kpool - 1
+    out.setdefault("indices", torch.empty((T, width), dtype=torch.int32, device=dev))
+    out.setdefault("scores", torch.empty((T, topk), dtype=torch.float32, device=dev))
+    out.setdefault("lengths", torch.empty((T,), dtype=torch.int32, device=dev))
+    if kpool > 1:
+        out.setdefault("pool_indices", torch.empty((T, topk), dtype=torch.int32, device=dev))
+    return out
+
+
+def score(q_op, k_op, w, cu_seqlens, max_seqlen, workspace, *, q_scale=None, k_scale=None, precision="bf16",
+          sm_scale=1.0, kpool=1, cu_pools=None):
+    """Scores of every causal candidate into ``workspace`` (row t at t*stride, see the C header)."""
+    lib = load()
+    prec = _prec(precision)
+    T, H, D = q_op.shape
+    S = k_op.shape[0]
+    for name, t in (("q_op", q_op), ("k_op", k_op), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale),
+                    ("cu_pools", cu_pools), ("workspace", workspace)):
+        _need(t, name)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,))
+    if w.dtype not in _DTYPES:
+        raise ValueError(f"w must be bf16 or fp32, got {w.dtype}")
+    st = lib.dsa_index_score(
+        _ptr(q_op), _ptr(q_scale), _ptr(k_op), _ptr(k_scale), _ptr(w), _DTYPES[w.dtype], T, S, H, D,
+        _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), int(kpool), _ptr(cu_pools), float(sm_scale),
+        prec, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q_op.device))
+    _check(st, "dsa_index_score")
+    return workspace
+
+
+def topk(workspace, T, cu_seqlens, max_seqlen, topk, *, kpool=1, cu_pools=None, kpool_tail=True, out=None):
+    """Per-row selection from the score rows ``score`` wrote; same outputs as ``score_topk``."""
+    lib = load()
+    _need(workspace, "workspace")
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,))
+    _need(cu_pools, "cu_pools")
+    out = _alloc_outputs(out, T, topk, kpool, workspace.device)
+    st = lib.dsa_index_topk(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), int(T), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, int(max_seqlen), int(kpool), _ptr(cu_pools), int(bool(kpool_tail)), int(topk),
+        _ptr(out["indices"]), _ptr(out["scores"]), _ptr(out["lengths"]), _ptr(out.get("pool_indices")),
+        _stream(workspace.device))
+    _check(st, "dsa_index_topk")
     return out

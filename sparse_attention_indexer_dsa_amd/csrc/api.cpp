@@ -165,6 +165,129 @@ size_t dsa_index_workspace_size(int32_t T, int32_t H, int32_t D, int32_t num_seq
   return (size_t)T * (size_t)stride * sizeof(float) + 256;
 }
 
+namespace {
+
+// Validation shared by the scoring and selection entry points. Fills `p` on success.
+dsa_status_t check_geometry(int T, const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int kpool,
+                            const int32_t* cu_pools, int topk, bool need_topk) {
+  if (T < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "T=%d must be non-negative", T);
+  if (need_topk && topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "topk=%d must be >= 1", topk);
+  if (kpool < 1 || kpool > 64) return fail(DSA_ERR_UNSUPPORTED, "kpool=%d must be within [1, 64]", kpool);
+  if (kpool > 1 && !cu_pools) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_pools is required when kpool > 1");
+  if (!cu_seqlens || num_seqs < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens must be given with num_seqs >= 1");
+  if (max_seqlen < 0 || (T > 0 && max_seqlen < 1))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_seqlen=%d must be >= 1", max_seqlen);
+  const int max_cand = max_candidates(max_seqlen, kpool);
+  if (need_topk) {
+    if (max_cand > dsa::kTopkMaxCand)
+      return fail(DSA_ERR_UNSUPPORTED, "%d candidates per row exceed the supported %d", max_cand, dsa::kTopkMaxCand);
+    if (dsa::topk_lds_bytes(max_cand, topk_p2(topk, max_cand)) > kMaxLds)
+      return fail(DSA_ERR_UNSUPPORTED, "topk=%d with %d candidates per row exceeds the on-chip selection buffer",
+                  topk, max_cand);
+    if ((long long)topk * kpool + kpool - 1 > 0x7FFFFFFFLL)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "topk*kpool overflows");
+  }
+  return DSA_OK;
+}
+
+dsa_status_t check_score_args(const void* q_op, const uint8_t* q_scale, const void* k_op, const uint8_t* k_scale,
+                              const void* w, dsa_dtype_t w_dtype, int T, int S, int H, int D, int precision,
+                              const void* workspace) {
+  dsa_status_t st;
+  if ((st = check_precision(precision)) != DSA_OK) return st;
+  if (w_dtype != DSA_DTYPE_BF16 && w_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "w_dtype %d must be bf16 (0) or fp32 (1)", (int)w_dtype);
+  if (T < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "T=%d and S=%d must be non-negative", T, S);
+  if ((st = check_hd(H, D, true)) != DSA_OK) return st;
+  if (T == 0) return DSA_OK;
+  const bool fp8 = precision != DSA_PREC_BF16;
+  if (!q_op || !w || !workspace) return fail(DSA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (S > 0 && !k_op) return fail(DSA_ERR_INVALID_ARGUMENT, "k_op is NULL");
+  if (fp8 && (!q_scale || (S > 0 && !k_scale)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale/k_scale are required for an fp8 precision");
+  if (!aligned(q_op, 16) || (k_op && !aligned(k_op, 16)) || !aligned(workspace, 256) ||
+      !aligned(w, w_dtype == DSA_DTYPE_FP32 ? 4 : 2))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned buffer (operands 16 B, workspace 256 B, weights 4 B)");
+  return DSA_OK;
+}
+
+dsa_status_t check_outputs(const int32_t* oi, const float* os, const int32_t* ol, const int32_t* op,
+                           const void* workspace) {
+  if (!oi || !os || !ol || !workspace) return fail(DSA_ERR_INVALID_ARGUMENT, "a required output pointer is NULL");
+  if (!aligned(oi, 4) || !aligned(os, 4) || !aligned(ol, 4) || (op && !aligned(op, 4)) || !aligned(workspace, 256))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned output (4 B) or workspace (256 B)");
+  return DSA_OK;
+}
+
+dsa::ScoreTopkLaunch make_launch(const void* q_op, const uint8_t* q_scale, const void* k_op, const uint8_t* k_scale,
+                                 const void* w, dsa_dtype_t w_dtype, int T, int S, int H, int D,
+                                 const int32_t* cu, int B, int max_seqlen, int kpool, const int32_t* cu_pools,
+                                 int kpool_tail, int topk, float sm_scale, int precision, int32_t* oi, float* os,
+                                 int32_t* ol, int32_t* op, const void* workspace) {
+  dsa::ScoreTopkLaunch p;
+  p.q_op = q_op; p.q_scale = q_scale; p.k_op = k_op; p.k_scale = k_scale;
+  p.w = w; p.w_bf16 = w_dtype == DSA_DTYPE_BF16;
+  p.T = T; p.S = S; p.H = H; p.D = D;
+  p.cu = cu; p.B = B; p.max_seqlen = max_seqlen;
+  p.kpool = kpool; p.cu_pools = cu_pools; p.kpool_tail = kpool_tail ? 1 : 0;
+  p.topk = topk; p.sm_scale = sm_scale; p.precision = precision;
+  p.out_indices = oi; p.out_scores = os; p.out_lengths = ol;
+  p.out_pool_indices = kpool > 1 ? op : nullptr;
+  p.scores = static_cast<float*>(const_cast<void*>(workspace));
+  const int max_cand = max_candidates(max_seqlen, kpool);
+  p.stride = row_stride(max_cand);
+  p.max_cand = max_cand;
+  return p;
+}
+
+}  // namespace
+
+dsa_status_t dsa_index_score(
+    const void* q_op, const uint8_t* q_scale,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools,
+    float sm_scale, dsa_precision_t precision,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_score_args(q_op, q_scale, k_op, k_scale, w, w_dtype, T, S, H, D, (int)precision, workspace)) != DSA_OK)
+    return st;
+  if ((st = check_geometry(T, cu_seqlens, num_seqs, max_seqlen, kpool, cu_pools, 1, false)) != DSA_OK) return st;
+  if (T == 0) return DSA_OK;
+  const size_t need = dsa_index_workspace_size(T, H, D, num_seqs, max_seqlen, 1, kpool, precision);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  dsa::ScoreTopkLaunch p = make_launch(q_op, q_scale, k_op, k_scale, w, w_dtype, T, S, H, D, cu_seqlens, num_seqs,
+                                       max_seqlen, kpool, cu_pools, 0, 1, sm_scale, (int)precision, nullptr, nullptr,
+                                       nullptr, nullptr, workspace);
+  hipError_t e = dsa::launch_score(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score");
+  return DSA_OK;
+}
+
+dsa_status_t dsa_index_topk(
+    const void* workspace, size_t workspace_bytes,
+    int32_t T, const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools, int32_t kpool_tail, int32_t topk,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths, int32_t* out_pool_indices,
+    hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_geometry(T, cu_seqlens, num_seqs, max_seqlen, kpool, cu_pools, topk, true)) != DSA_OK) return st;
+  if (T == 0) return DSA_OK;
+  if ((st = check_outputs(out_indices, out_scores, out_lengths, out_pool_indices, workspace)) != DSA_OK) return st;
+  const size_t need = dsa_index_workspace_size(T, 0, 0, num_seqs, max_seqlen, topk, kpool, DSA_PREC_BF16);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  dsa::ScoreTopkLaunch p = make_launch(nullptr, nullptr, nullptr, nullptr, nullptr, DSA_DTYPE_FP32, T, 0, 0, 0,
+                                       cu_seqlens, num_seqs, max_seqlen, kpool, cu_pools, kpool_tail, topk, 1.0f,
+                                       0, out_indices, out_scores, out_lengths, out_pool_indices, workspace);
+  hipError_t e = dsa::launch_topk(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_topk");
+  return DSA_OK;
+}
+
 dsa_status_t dsa_index_score_topk(
     const void* q_op, const uint8_t* q_scale,
     const void* k_op, const uint8_t* k_scale,
@@ -177,52 +300,17 @@ dsa_status_t dsa_index_score_topk(
     int32_t* out_pool_indices,
     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   dsa_status_t st;
-  if ((st = check_precision((int)precision)) != DSA_OK) return st;
-  if (w_dtype != DSA_DTYPE_BF16 && w_dtype != DSA_DTYPE_FP32)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "w_dtype %d must be bf16 (0) or fp32 (1)", (int)w_dtype);
-  if (T < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "T=%d and S=%d must be non-negative", T, S);
-  if ((st = check_hd(H, D, true)) != DSA_OK) return st;
-  if (topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "topk=%d must be >= 1", topk);
-  if (kpool < 1 || kpool > 64) return fail(DSA_ERR_UNSUPPORTED, "kpool=%d must be within [1, 64]", kpool);
-  if (kpool > 1 && !cu_pools) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_pools is required when kpool > 1");
-  if (!cu_seqlens || num_seqs < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens must be given with num_seqs >= 1");
-  if (max_seqlen < 0 || (T > 0 && max_seqlen < 1))
-    return fail(DSA_ERR_INVALID_ARGUMENT, "max_seqlen=%d must be >= 1", max_seqlen);
+  if ((st = check_score_args(q_op, q_scale, k_op, k_scale, w, w_dtype, T, S, H, D, (int)precision, workspace)) != DSA_OK)
+    return st;
+  if ((st = check_geometry(T, cu_seqlens, num_seqs, max_seqlen, kpool, cu_pools, topk, true)) != DSA_OK) return st;
   if (T == 0) return DSA_OK;
-  const bool fp8 = precision != DSA_PREC_BF16;
-  if (!q_op || !w || !out_indices || !out_scores || !out_lengths || !workspace)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-  if (S > 0 && !k_op) return fail(DSA_ERR_INVALID_ARGUMENT, "k_op is NULL");
-  if (fp8 && (!q_scale || (S > 0 && !k_scale)))
-    return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale/k_scale are required for an fp8 precision");
-  if (!aligned(q_op, 16) || (k_op && !aligned(k_op, 16)) || !aligned(workspace, 256) ||
-      !aligned(w, w_dtype == DSA_DTYPE_FP32 ? 4 : 2) || !aligned(out_indices, 4) || !aligned(out_scores, 4) ||
-      !aligned(out_lengths, 4) || (out_pool_indices && !aligned(out_pool_indices, 4)))
-    return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned buffer (operands 16 B, workspace 256 B, outputs 4 B)");
-  const int max_cand = max_candidates(max_seqlen, kpool);
-  if (max_cand > dsa::kTopkMaxCand)
-    return fail(DSA_ERR_UNSUPPORTED, "%d candidates per row exceed the supported %d", max_cand, dsa::kTopkMaxCand);
-  if (dsa::topk_lds_bytes(max_cand, topk_p2(topk, max_cand)) > kMaxLds)
-    return fail(DSA_ERR_UNSUPPORTED, "topk=%d with %d candidates per row exceeds the on-chip selection buffer",
-                topk, max_cand);
-  if ((long long)topk * kpool + kpool - 1 > 0x7FFFFFFFLL)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "topk*kpool overflows");
+  if ((st = check_outputs(out_indices, out_scores, out_lengths, out_pool_indices, workspace)) != DSA_OK) return st;
   const size_t need = dsa_index_workspace_size(T, H, D, num_seqs, max_seqlen, topk, kpool, precision);
   if (workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-
-  dsa::ScoreTopkLaunch p;
-  p.q_op = q_op; p.q_scale = q_scale; p.k_op = k_op; p.k_scale = k_scale;
-  p.w = w; p.w_bf16 = w_dtype == DSA_DTYPE_BF16;
-  p.T = T; p.S = S; p.H = H; p.D = D;
-  p.cu = cu_seqlens; p.B = num_seqs; p.max_seqlen = max_seqlen;
-  p.kpool = kpool; p.cu_pools = cu_pools; p.kpool_tail = kpool_tail ? 1 : 0;
-  p.topk = topk; p.sm_scale = sm_scale; p.precision = (int)precision;
-  p.out_indices = out_indices; p.out_scores = out_scores; p.out_lengths = out_lengths;
-  p.out_pool_indices = kpool > 1 ? out_pool_indices : nullptr;
-  p.scores = static_cast<float*>(workspace);
-  p.stride = row_stride(max_cand);
-  p.max_cand = max_cand;
+  dsa::ScoreTopkLaunch p = make_launch(q_op, q_scale, k_op, k_scale, w, w_dtype, T, S, H, D, cu_seqlens, num_seqs,
+                                       max_seqlen, kpool, cu_pools, kpool_tail, topk, sm_scale, (int)precision,
+                                       out_indices, out_scores, out_lengths, out_pool_indices, workspace);
   hipError_t e = dsa::launch_score(p, stream);
   if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk (score)");
   e = dsa::launch_topk(p, stream);

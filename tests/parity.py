@@ -266,12 +266,12 @@ def sample_rows(inp, topk, kp, n_random=16, seed=0):
     return sorted(rows)
 
 
-def oracle_operands_rows(inp, cfg, rows):
-    """Oracle operands of the sampled query rows (dict t -> values) and of all keys."""
+def oracle_operands_rows(inp, cfg, rows, keys=True):
+    """Oracle operands of the sampled query rows (dict t -> values) and, if ``keys``, of all keys."""
     prec, kp = cfg["precision"], cfg.get("kpool", 1)
     rows = np.asarray(rows, np.int64)
     q32 = gen.bf16_bits_to_f32(inp["q"][rows])
-    k32 = gen.bf16_bits_to_f32(inp["k"])
+    k32 = gen.bf16_bits_to_f32(inp["k"]) if keys else None
     if cfg.get("preprocess"):
         qc, kc = orc.preprocess(q32, k32, inp["cu_seqlens"],
                                 gamma=inp.get("gamma") if cfg.get("layernorm") else None,
@@ -285,6 +285,8 @@ def oracle_operands_rows(inp, cfg, rows):
     o["q_op"], o["q_scale"] = orc.quantize(qc, prec)
     qd = orc.dequantize(o["q_op"], o["q_scale"], prec)
     o["q_deq"] = {int(t): qd[i] for i, t in enumerate(rows)}
+    if not keys:
+        return o
     if kp > 1:
         pooled, cu_pools = orc.kpool(kc, inp["cu_seqlens"], inp["gate"], inp["bias"], kp)
         o["pooled"], o["pooled_scale"] = orc.quantize(pooled, prec)
