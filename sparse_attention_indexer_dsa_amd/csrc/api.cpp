@@ -10,7 +10,7 @@
 #include "launch.h"
 
 namespace dsa {
-size_t topk_lds_bytes(int max_cand, int p2);
+size_t topk_lds_bytes(int max_cand, int topk);
 }
 
 namespace {
@@ -55,12 +55,6 @@ int max_candidates(int max_seqlen, int kpool) { return kpool == 1 ? max_seqlen :
 int row_stride(int max_cand) {
   const int c = max_cand < 1 ? 1 : max_cand;
   return (c + 63) / 64 * 64;
-}
-
-int topk_p2(int topk, int max_cand) {
-  int p2 = 1;
-  while (p2 < topk && p2 < max_cand) p2 <<= 1;
-  return p2;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
@@ -181,7 +175,7 @@ dsa_status_t check_geometry(int T, const int32_t* cu_seqlens, int num_seqs, int 
   if (need_topk) {
     if (max_cand > dsa::kTopkMaxCand)
       return fail(DSA_ERR_UNSUPPORTED, "%d candidates per row exceed the supported %d", max_cand, dsa::kTopkMaxCand);
-    if (dsa::topk_lds_bytes(max_cand, topk_p2(topk, max_cand)) > kMaxLds)
+    if (dsa::topk_lds_bytes(max_cand, topk) > kMaxLds)
       return fail(DSA_ERR_UNSUPPORTED, "topk=%d with %d candidates per row exceeds the on-chip selection buffer",
                   topk, max_cand);
     if ((long long)topk * kpool + kpool - 1 > 0x7FFFFFFFLL)

@@ -1,13 +1,17 @@
 // Per-row top-k selection over the score workspace, with KPool expansion (gfx950).
 //
-// Each workgroup owns one query row. The row's candidate scores are loaded into LDS as
-// order-preserving uint32 keys; a three-pass radix select (11 + 11 + 10 bits, LDS
-// histograms with integer atomics) finds the k-th largest key; candidates above it are
-// taken, and among candidates equal to it the lowest indices are taken (deterministic
-// tie breaking, Megatron-LM PR 5992, "Key changes"). The selection is then sorted by
-// (score descending, index ascending) with a bitonic sort in LDS and written with -1 /
-// -inf padding. For KPool (PR 7522, "Changes") the selected pools are expanded to their
-// tokens and the query's incomplete causal pool is appended when requested.
+// One workgroup per query row. Each thread holds a contiguous chunk of the row's
+// candidates as order-preserving uint32 keys in registers. A three-pass radix select
+// (11 + 11 + 10 bits; LDS histograms with integer atomics, bin search by wave scans) finds
+// the topk-th largest key; every candidate above it is taken and, among candidates equal
+// to it, the lowest indices (deterministic tie breaking, Megatron-LM PR 5992, "Key
+// changes"). Positions in the selection buffer come from block prefix sums, so the
+// kernel uses no floating-point atomics and its result does not depend on scheduling.
+// The selection is sorted by (score descending, index ascending) with a bitonic network
+// whose stages inside a 64- or 256-element segment run in registers (lane shuffles and
+// in-lane exchanges) and only the wider stages go through LDS. Outputs are padded with
+// -1 / -inf. For KPool (PR 7522, "Changes") selected pools are expanded to their tokens
+// and the query's incomplete causal pool is appended when requested.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -18,166 +22,562 @@
 namespace dsa {
 namespace {
 
-constexpr int kNT = 256;
-
 struct TopkArgs {
   const float* scores; int stride; int max_cand;
-  int T, B, max_seqlen, kpool, kpool_tail, topk, p2;
+  int T, B, max_seqlen, kpool, kpool_tail, topk, p2max;
   const int32_t* cu; const int32_t* cu_pools;
   int32_t* out_indices; float* out_scores; int32_t* out_lengths; int32_t* out_pool_indices;
 };
 
-// Inclusive suffix sum over kNT per-thread values (result: sum of values of threads >= tid).
-__device__ __forceinline__ int block_suffix_sum(int v, int* buf) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kNT; off <<= 1) {
-    const int o = tid + off < kNT ? buf[tid + off] : 0;
-    __syncthreads();
-    buf[tid] += o;
-    __syncthreads();
+typedef unsigned long long u64;
+
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((u64)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts (within rows of 16
+// lanes) and the row broadcasts of lanes 15 and 31 (across rows).
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Inclusive suffix sum over the 64 lanes of a wave (lane l gets the sum over lanes >= l).
+__device__ __forceinline__ int wave_suffix_sum(int v) {
+  const int incl = wave_prefix_sum(v);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  return total - incl + v;
+}
+
+// Bitonic stages with distance j < 64*V inside one register-resident segment of 64*V
+// elements: x[v] holds element seg_base + 64 v + lane. Direction of position i: up when
+// (i & k) == 0. Runs stages j = j0, j0/2, ..., 1.
+template <int V, int JV>
+__device__ __forceinline__ void inlane_stage(u64 (&x)[V], int seg_base, int k) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    if ((v & JV) == 0) {
+      const int i = seg_base + 64 * v + lane;
+      const bool up = (i & k) == 0;
+      const u64 a = x[v], b = x[v + JV];
+      const bool sw = (a > b) == up;
+      x[v] = sw ? b : a;
+      x[v + JV] = sw ? a : b;
+    }
   }
-  const int r = buf[tid];
+}
+
+template <int V>
+__device__ __forceinline__ void segment_stages(u64 (&x)[V], int seg_base, int k, int j0) {
+  const int lane = threadIdx.x & 63;
+  for (int j = j0; j >= 1; j >>= 1) {
+    if (j >= 64) {
+      // in-lane exchanges between slots v and v + j/64 (register indices fixed at compile time)
+      if (V >= 4 && j == 128) inlane_stage<V, (V >= 4 ? 2 : 0)>(x, seg_base, k);
+      else if (V >= 2) inlane_stage<V, (V >= 2 ? 1 : 0)>(x, seg_base, k);
+    } else {
+      const bool lower = (lane & j) == 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int i = seg_base + 64 * v + lane;
+        const bool up = (i & k) == 0;
+        const u64 y = shfl_xor_u64(x[v], j);
+        const u64 mn = x[v] < y ? x[v] : y, mx = x[v] < y ? y : x[v];
+        x[v] = (lower == up) ? mn : mx;
+      }
+    }
+  }
+}
+
+// Ascending bitonic sort of sel[0, n2) (n2 a power of two >= 64) by the whole workgroup.
+template <int V, int NT>
+__device__ __forceinline__ void bitonic_sort(u64* sel, int n2) {
+  constexpr int NW = NT / 64;
+  constexpr int SEG = 64 * V;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nseg = n2 / SEG;
+  // 1) every segment sorted on its own (k = 2 .. SEG), alternating directions as the
+  //    bitonic network requires (direction comes from the global position)
+  for (int s = wv; s < nseg; s += NW) {
+    u64 x[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = sel[s * SEG + 64 * v + lane];
+    for (int k = 2; k <= SEG; k <<= 1) segment_stages<V>(x, s * SEG, k, k >> 1);
+#pragma unroll
+    for (int v = 0; v < V; ++v) sel[s * SEG + 64 * v + lane] = x[v];
+  }
+  // 2) merges wider than a segment: the stages j >= SEG in LDS, the rest in registers
+  for (int k = 2 * SEG; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j >= SEG; j >>= 1) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < n2; i += NT) {
+        const int p = i ^ j;
+        if (p > i) {
+          const bool up = (i & k) == 0;
+          const u64 a = sel[i], b = sel[p];
+          if ((a > b) == up) { sel[i] = b; sel[p] = a; }
+        }
+      }
+    }
+    __syncthreads();
+    for (int s = wv; s < nseg; s += NW) {
+      u64 x[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) x[v] = sel[s * SEG + 64 * v + lane];
+      segment_stages<V>(x, s * SEG, k, SEG >> 1);
+#pragma unroll
+      for (int v = 0; v < V; ++v) sel[s * SEG + 64 * v + lane] = x[v];
+    }
+  }
   __syncthreads();
+}
+
+// Wave-wide max (MAX) or min of a uint32 with DPP steps; the result is valid in every lane.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme(uint32_t x) {
+  const int id = MAX ? 0 : -1;
+  int v = (int)x;
+#define DSA_STEP(ctrl, rm)                                                        \
+  {                                                                               \
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(id, v, ctrl, rm, 0xf, false); \
+    const uint32_t c = (uint32_t)v;                                               \
+    v = (int)(MAX ? (o > c ? o : c) : (o < c ? o : c));                           \
+  }
+  DSA_STEP(0x111, 0xf) DSA_STEP(0x112, 0xf) DSA_STEP(0x114, 0xf) DSA_STEP(0x118, 0xf)
+  DSA_STEP(0x142, 0xa) DSA_STEP(0x143, 0xc)
+#undef DSA_STEP
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+
+// Block-wide min and max of one uint32 pair per thread (results valid in every thread).
+// Uses buf[2*NW].
+template <int NT>
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, int* buf) {
+  constexpr int NW = NT / 64;
+  mn = wave_extreme<false>(mn);
+  mx = wave_extreme<true>(mx);
+  if (NW == 1) return;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { buf[threadIdx.x >> 6] = (int)mn; buf[NW + (threadIdx.x >> 6)] = (int)mx; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t a = (uint32_t)buf[w], b = (uint32_t)buf[NW + w];
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+}
+
+// Exclusive prefix sum of one int per thread over the block (in thread order); `tot` gets
+// the block total. Uses wsum[NW] (NW <= 16, 16-byte aligned).
+template <int NT>
+__device__ __forceinline__ int block_exclusive_sum(int v, int* wsum, int& tot) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int incl = wave_prefix_sum(v);
+  __syncthreads();
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = incl - v;
+  tot = 0;
+  if (NW == 1) {
+    tot = wsum[0];
+  } else {
+#pragma unroll
+    for (int w4 = 0; w4 < (NW + 3) / 4; ++w4) {
+      const int4 q = reinterpret_cast<const int4*>(wsum)[w4];
+      const int qa[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = 4 * w4 + j;
+        if (w < NW) { if (w < wv) before += qa[j]; tot += qa[j]; }
+      }
+    }
+  }
+  return before;
+}
+
+// Finds the bin of a descending rank inside a histogram of NB bins (NB % NT == 0): the bin
+// d with above(d) < krem <= above(d) + hist[d], above(d) = count in bins > d. Thread tid
+// owns bins [tid*PER, tid*PER + PER), so higher bins live in higher threads. Returns d in
+// misc[0], above(d) in misc[1] and hist[d] in misc[2] (valid in every thread afterwards).
+template <int NT, int NB>
+__device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int krem, int* wsum, int* misc) {
+  constexpr int NW = NT / 64;
+  constexpr int PER = NB / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t h[PER];
+  if (PER >= 4) {
+#pragma unroll
+    for (int j = 0; j < PER; j += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(hist + tid * PER + j);
+      h[j] = q.x; h[j + 1] = q.y; h[j + 2] = q.z; h[j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) h[j] = hist[tid * PER + j];
+  }
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) mine += (int)h[j];
+  const int suf = wave_suffix_sum(mine);
+  if (lane == 0) wsum[wv] = suf;
+  __syncthreads();
+  int above = suf - mine;
+  if (NW > 1) {
+#pragma unroll
+    for (int w4 = 0; w4 < (NW + 3) / 4; ++w4) {
+      const int4 q = reinterpret_cast<const int4*>(wsum)[w4];
+      const int qa[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = 4 * w4 + j;
+        if (w < NW && w > wv) above += qa[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = PER - 1; j >= 0; --j) {
+    const int hc = (int)h[j];
+    if (above < krem && krem <= above + hc) { misc[0] = tid * PER + j; misc[1] = above; misc[2] = hc; }
+    above += hc;
+  }
+  __syncthreads();
+}
+
+constexpr int kValueList = 64;   // a threshold bin this small is resolved by counting
+constexpr int kBuckets = 1024;   // buckets of the ordering pass
+constexpr int kBucketMax = 64;   // larger buckets (heavy ties) fall back to the bitonic network
+
+struct RowInfo {
+  int t, b, lo, u, cand, nsel;
+};
+
+__device__ __forceinline__ RowInfo row_info(const TopkArgs& a, int t) {
+  RowInfo r;
+  r.t = t;
+  r.b = find_doc(a.cu, a.B, t);
+  r.lo = clampi(a.cu[r.b], 0, a.T);
+  r.u = max(0, min(t - r.lo, a.max_seqlen - 1));
+  r.cand = min((r.u + 1) / a.kpool, a.max_cand);
+  r.nsel = min(a.topk, r.cand);
   return r;
 }
 
-__global__ __launch_bounds__(kNT) void topk_kernel(TopkArgs a) {
+// Scores of this thread's chunk [tid*EPT, tid*EPT + EPT) of row r (NaN marks "no candidate").
+template <int EPT>
+__device__ __forceinline__ void load_row(const TopkArgs& a, const RowInfo& r, float (&x)[EPT]) {
+  const float* row = a.scores + (long long)r.t * a.stride;
+  const int i0 = threadIdx.x * EPT;
+  if (EPT % 4 == 0 && i0 + EPT <= r.cand) {
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i0 + e);
+      x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) x[e] = (i0 + e < r.cand) ? row[i0 + e] : __builtin_nanf("");
+  }
+}
+
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  unsigned long long* sel = reinterpret_cast<unsigned long long*>(smem);          // [p2]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(sel + a.p2);                        // [2048]
-  int* scan = reinterpret_cast<int*>(hist + 2048);                                 // [kNT]
-  int* misc = scan + kNT;                                                          // [4]
-  uint32_t* keys = reinterpret_cast<uint32_t*>(misc + 4);                          // [max_cand]
+  u64* selA = reinterpret_cast<u64*>(smem);                                  // [p2max]
+  u64* selB = selA + a.p2max;                                                // [p2max]
+  uint32_t* aux = reinterpret_cast<uint32_t*>(selB + a.p2max);               // [kBuckets]
+  uint32_t* hist = aux + kBuckets;                                           // [2048]
+  int* wsum = reinterpret_cast<int*>(hist + 2048);                           // [32]
+  int* misc = wsum + 32;                                                     // [8]
 
   const int tid = threadIdx.x;
-  const int t = blockIdx.x;
-  const int b = find_doc(a.cu, a.B, t);
-  const int lo = clampi(a.cu[b], 0, a.T);
-  const int u = max(0, min(t - lo, a.max_seqlen - 1));
-  const int kp = a.kpool;
-  const int cand = min((u + 1) / kp, a.max_cand);
+  const int i0 = tid * EPT;
   const int topk = a.topk;
-  const int nsel = min(topk, cand);
-  const float* row = a.scores + (long long)t * a.stride;
+  const int kp = a.kpool;
+  const int t = blockIdx.x;
+  const RowInfo cur = row_info(a, t);
+  const int cand = cur.cand, nsel = cur.nsel;
 
-  for (int i = tid; i < cand; i += kNT) keys[i] = score_key(row[i]);
-  __syncthreads();
-
-  if (cand <= topk) {
-    for (int i = tid; i < cand; i += kNT)
-      sel[i] = ((unsigned long long)(~keys[i]) << 32) | (uint32_t)i;
-  } else {
-    // ---- radix select of the topk-th largest key
-    uint32_t prefix = 0, pmask = 0;
-    int krem = topk;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int nbins = pass == 2 ? 1024 : 2048;
-      for (int i = tid; i < nbins; i += kNT) hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < cand; i += kNT) {
-        const uint32_t k = keys[i];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1u);
-      }
-      __syncthreads();
-      const int per = nbins / kNT;
-      int mine = 0;
-      for (int j = 0; j < per; ++j) mine += hist[tid * per + j];
-      const int incl = block_suffix_sum(mine, scan);
-      int above = incl - mine;                   // count in bins above this thread's range
-      for (int j = per - 1; j >= 0; --j) {
-        const int bin = tid * per + j;
-        const int hcount = hist[bin];
-        if (above < krem && krem <= above + hcount) { misc[0] = bin; misc[1] = above; }
-        above += hcount;
-      }
-      __syncthreads();
-      const int digit = misc[0];
-      krem -= misc[1];
-      prefix |= (uint32_t)digit << shift;
-      pmask |= (uint32_t)(nbins - 1) << shift;
-      __syncthreads();
-    }
-    const uint32_t thr = prefix;                 // the topk-th largest key; krem copies of it are taken
-    // ---- compaction: keys above thr anywhere in [0, topk-krem); ties in index order after them
-    const int chunk = (cand + kNT - 1) / kNT;
-    const int i0 = min(cand, tid * chunk), i1 = min(cand, i0 + chunk);
-    int ties = 0;
-    for (int i = i0; i < i1; ++i) ties += keys[i] == thr;
-    const int incl = block_suffix_sum(ties, scan);
-    // ties of threads before this one = total - inclusive suffix
-    if (tid == 0) { misc[2] = incl; misc[3] = 0; }
-    __syncthreads();
-    int rank = misc[2] - incl;
-    const int ngt = topk - krem;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t k = keys[i];
-      const unsigned long long v = ((unsigned long long)(~k) << 32) | (uint32_t)i;
-      if (k > thr) {
-        const int pos = atomicAdd(&misc[3], 1);
-        sel[pos] = v;
-      } else if (k == thr) {
-        if (rank < krem) sel[ngt + rank] = v;
-        ++rank;
-      }
-    }
+  uint32_t key[EPT];                       // order-preserving keys (0: no candidate)
+  {
+    float raw[EPT];
+    load_row<EPT>(a, cur, raw);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) key[e] = (i0 + e < cand) ? score_key(raw[e]) : 0u;
   }
-  for (int i = nsel + tid; i < a.p2; i += kNT) sel[i] = ~0ull;
-  __syncthreads();
 
-  // ---- bitonic sort (ascending on ~key:index = score descending, index ascending)
-  int n2 = 1;
-  while (n2 < nsel) n2 <<= 1;
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += kNT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = sel[i], y = sel[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) { sel[i] = y; sel[ixj] = x; }
+  // ---- key range of the row's candidates (max and min in one reduction)
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (key[e] != 0u) { kmax = key[e] > kmax ? key[e] : kmax; kmin = key[e] < kmin ? key[e] : kmin; }
+  }
+  block_minmax<NT>(kmin, kmax, wsum);
+
+  uint32_t thr = kmin;   // every selected key is >= thr
+  int krem = 0;          // candidates equal to thr that are taken (lowest indices first)
+  const float vmin = key_score(kmin), vmax = key_score(kmax);
+  if (cand > topk) {
+    krem = topk;
+    bool resolved = false;
+    // ---- pass 1: 2048 bins linear in the score over [vmin, vmax]. Bins are monotone in the
+    //      score, and a smooth score distribution spreads evenly over them, so the LDS
+    //      atomics rarely collide and the threshold bin holds few candidates.
+    const float span = vmax - vmin;
+    if (span > 0.f && span < INFINITY) {
+      const float vscale = 2048.f / span;
+      int bin[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) bin[e] = key[e] != 0u ? min(2047, (int)((key_score(key[e]) - vmin) * vscale)) : -1;
+      for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+      if (tid == 0) misc[5] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        if (bin[e] >= 0) atomicAdd(&hist[bin[e]], 1u);
+      __syncthreads();
+      find_rank_bin<NT, 2048>(hist, krem, wsum, misc);
+      const int d1 = misc[0];
+      const int c1 = misc[2];
+      const int krem1 = krem - misc[1];
+      if (c1 <= kValueList) {
+        // the threshold bin's candidates to a list (order irrelevant), then one wave finds
+        // the krem1-th largest among them by counting over lane values
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+          if (bin[e] == d1) aux[atomicAdd(&misc[5], 1)] = key[e];
+        __syncthreads();
+        if (tid < 64) {
+          const uint32_t k = tid < c1 ? aux[tid] : 0u;
+          int gt = 0, ge = 0;
+          for (int q = 0; q < c1; ++q) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)k, q);
+            gt += o > k;
+            ge += o >= k;
+          }
+          const bool hit = tid < c1 && gt < krem1 && krem1 <= ge;
+          const u64 m = __ballot(hit);
+          const int src = __ffsll((long long)m) - 1;
+          const uint32_t fk = __shfl(k, src, 64);
+          const int fg = __shfl(gt, src, 64);
+          if (tid == 0) { misc[3] = (int)fk; misc[4] = krem1 - fg; }
         }
+        __syncthreads();
+        thr = (uint32_t)misc[3];
+        krem = misc[4];
+        resolved = true;
       }
-      __syncthreads();
+    }
+    if (!resolved) {
+      // ---- clustered rows: radix select on the key bits (11 + 11 + 10)
+      uint32_t prefix = 0, pmask = 0;
+      krem = topk;
+#pragma unroll 1
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nbins = pass == 2 ? 1024 : 2048;
+        __syncthreads();
+        for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          const uint32_t k = key[e];
+          if (k != 0u && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+        }
+        __syncthreads();
+        find_rank_bin<NT, 2048>(hist, krem, wsum, misc);
+        krem -= misc[1];
+        prefix |= (uint32_t)misc[0] << shift;
+        pmask |= (uint32_t)(nbins - 1) << shift;
+      }
+      thr = prefix;
+    }
+  } else {
+    krem = cand;   // every candidate is taken
+  }
+
+  // ---- compaction in index order: keys above thr, then the first krem keys equal to thr.
+  //      Positions come from one block prefix sum of (above << 16 | equal) counts.
+  int packed = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) packed += key[e] > thr ? (1 << 16) : ((key[e] == thr && key[e] != 0u) ? 1 : 0);
+  int tot;
+  const int before = block_exclusive_sum<NT>(packed, wsum, tot);
+  {
+    const int ngt = tot >> 16;
+    int pos_gt = before >> 16;
+    int rank_eq = before & 0xFFFF;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t k = key[e];
+      const u64 v = ((u64)(~k) << 32) | (uint32_t)(i0 + e);
+      if (k > thr) {
+        selB[pos_gt++] = v;
+      } else if (k == thr && k != 0u) {
+        if (rank_eq < krem) selB[ngt + rank_eq] = v;
+        ++rank_eq;
+      }
     }
   }
+
+  // ---- ordering of selB[0, nsel): bucket b = floor((vmax - score) * scale) over
+  //      [score(thr), vmax] (ascending b = descending score); counts, starts by a prefix
+  //      sum, scatter, then each entry's exact rank inside its bucket
+  const float vthr = key_score(thr);
+  const float ospan = vmax - vthr;
+  const float oscale = (ospan > 0.f && ospan < INFINITY) ? (float)(kBuckets - 1) / ospan : 0.f;
+  constexpr int SPT = 8;                   // selected entries per thread handled in registers
+  uint32_t* cnt = hist;                    // [kBuckets]
+  uint32_t* start = hist + kBuckets;       // [kBuckets]
+  uint32_t* fill = aux;                    // [kBuckets]
+  for (int i = tid; i < kBuckets; i += NT) cnt[i] = 0;
+  __syncthreads();
+  u64 mine_v[SPT];
+  int mine_b[SPT];
+  const int nmine = (nsel - tid + NT - 1) / NT;   // entries tid, tid + NT, ...
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int i = tid + j * NT;
+    mine_b[j] = -1;
+    if (j < nmine) {
+      mine_v[j] = selB[i];
+      mine_b[j] = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(mine_v[j] >> 32))) * oscale));
+      atomicAdd(&cnt[mine_b[j]], 1u);
+    }
+  }
+  for (int i = tid + SPT * NT; i < nsel; i += NT) {      // beyond the register share
+    const int bk = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(selB[i] >> 32))) * oscale));
+    atomicAdd(&cnt[bk], 1u);
+  }
+  __syncthreads();
+  {
+    constexpr int PER = kBuckets / NT > 0 ? kBuckets / NT : 1;
+    uint32_t c[PER];
+    int m = 0, big = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int bk = tid * PER + j;
+      c[j] = bk < kBuckets ? cnt[bk] : 0u;
+      m += (int)c[j];
+      big |= c[j] > (uint32_t)kBucketMax;
+    }
+    int btot;
+    int run = block_exclusive_sum<NT>(m, wsum, btot);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int bk = tid * PER + j;
+      if (bk < kBuckets) { start[bk] = run; fill[bk] = run; run += (int)c[j]; }
+    }
+    if (tid == 0) misc[2] = 0;
+    __syncthreads();
+    if (big) misc[2] = 1;
+  }
+  __syncthreads();
+  u64* tmp = selA;
+  const bool heavy = misc[2] != 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if (mine_b[j] >= 0) tmp[atomicAdd(&fill[mine_b[j]], 1u)] = mine_v[j];
+  for (int i = tid + SPT * NT; i < nsel; i += NT) {
+    const u64 v = selB[i];
+    const int bk = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(v >> 32))) * oscale));
+    tmp[atomicAdd(&fill[bk], 1u)] = v;
+  }
+  __syncthreads();
+  int n2 = 64;
+  while (n2 < nsel) n2 <<= 1;
+  if (heavy) {
+    // heavy ties / clustering: the bitonic network on the whole selection
+    for (int i = nsel + tid; i < n2; i += NT) tmp[i] = ~0ull;
+    __syncthreads();
+    if (n2 <= 128) bitonic_sort<1, NT>(tmp, n2);
+    else bitonic_sort<4, NT>(tmp, n2);
+  } else {
+    for (int i = tid; i < nsel; i += NT) {
+      const u64 v = tmp[i];
+      const int bk = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(v >> 32))) * oscale));
+      const int s0 = start[bk], n = cnt[bk];
+      int r = 0;
+      for (int q = 0; q < n; ++q) r += tmp[s0 + q] < v;
+      selB[s0 + r] = v;
+    }
+    __syncthreads();
+  }
+  const u64* sel = heavy ? tmp : selB;
 
   // ---- outputs
+  const int lo = cur.lo, u = cur.u, b = cur.b;
   float* os = a.out_scores + (long long)t * topk;
-  for (int j = tid; j < topk; j += kNT)
+  for (int j = tid; j < topk; j += NT)
     os[j] = j < nsel ? key_score(~(uint32_t)(sel[j] >> 32)) : -INFINITY;
   if (kp == 1) {
     int32_t* oi = a.out_indices + (long long)t * topk;
-    for (int j = tid; j < topk; j += kNT) oi[j] = j < nsel ? lo + (int)(uint32_t)sel[j] : -1;
+    for (int j = tid; j < topk; j += NT) oi[j] = j < nsel ? lo + (int)(uint32_t)sel[j] : -1;
     if (tid == 0) a.out_lengths[t] = nsel;
   } else {
     const int pbase = a.cu_pools[b];
     if (a.out_pool_indices) {
       int32_t* op = a.out_pool_indices + (long long)t * topk;
-      for (int j = tid; j < topk; j += kNT) op[j] = j < nsel ? pbase + (int)(uint32_t)sel[j] : -1;
+      for (int j = tid; j < topk; j += NT) op[j] = j < nsel ? pbase + (int)(uint32_t)sel[j] : -1;
     }
     const int tail = a.kpool_tail ? (u + 1) % kp : 0;
     const int width = topk * kp + kp - 1;
     const int npool_tok = nsel * kp;
     const int tail_start = lo + (u / kp) * kp;
     int32_t* oi = a.out_indices + (long long)t * width;
-    for (int s = tid; s < width; s += kNT) {
+    for (int s2 = tid; s2 < width; s2 += NT) {
       int v = -1;
-      if (s < npool_tok) v = lo + (int)(uint32_t)sel[s / kp] * kp + s % kp;
-      else if (s < npool_tok + tail) v = tail_start + (s - npool_tok);
-      oi[s] = v;
+      if (s2 < npool_tok) v = lo + (int)(uint32_t)sel[s2 / kp] * kp + s2 % kp;
+      else if (s2 < npool_tok + tail) v = tail_start + (s2 - npool_tok);
+      oi[s2] = v;
     }
     if (tid == 0) a.out_lengths[t] = npool_tok + tail;
   }
 }
 
+template <int NT, int EPT>
+hipError_t launch_cfg(const TopkArgs& a, size_t lds, hipStream_t st) {
+  // The dynamic LDS limit is raised only when a launch needs more than the default 64 KB,
+  // and only to what it needs: the raised limit is what each workgroup reserves, so a
+  // blanket 160 KB would leave one workgroup per CU. Done once per (device, size) and
+  // never inside graph capture (it is not a stream operation).
+  if (lds > 64 * 1024) {
+    static std::mutex mu;
+    static size_t set_to[64] = {0};
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (device >= 64 || set_to[device] != lds) {
+      e = hipFuncSetAttribute((const void*)topk_kernel<NT, EPT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      if (device < 64) set_to[device] = lds;
+    }
+  }
+  hipLaunchKernelGGL((topk_kernel<NT, EPT>), dim3(a.T), dim3(NT), lds, st, a);
+  return hipGetLastError();
+}
+
+int p2_of(int topk, int max_cand) {
+  int p2 = 64;
+  while (p2 < topk && p2 < max_cand) p2 <<= 1;
+  return p2;
+}
+
 }  // namespace
 
-size_t topk_lds_bytes(int max_cand, int p2) {
-  return (size_t)p2 * 8 + 2048 * 4 + kNT * 4 + 16 + (size_t)max_cand * 4;
+size_t topk_lds_bytes(int max_cand, int topk) {
+  return (size_t)p2_of(topk, max_cand) * 8 * 2 + (size_t)kBuckets * 4 + 2048 * 4 + 32 * 4 + 8 * 4;
 }
 
 hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
@@ -186,30 +586,20 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
   a.scores = p.scores; a.stride = p.stride; a.max_cand = p.max_cand;
   a.T = p.T; a.B = p.B; a.max_seqlen = p.max_seqlen; a.kpool = p.kpool; a.kpool_tail = p.kpool_tail;
   a.topk = p.topk;
-  int p2 = 1;
-  while (p2 < p.topk && p2 < p.max_cand) p2 <<= 1;
-  a.p2 = p2;
+  a.p2max = p2_of(p.topk, p.max_cand);
   a.cu = p.cu; a.cu_pools = p.cu_pools;
   a.out_indices = p.out_indices; a.out_scores = p.out_scores; a.out_lengths = p.out_lengths;
   a.out_pool_indices = p.out_pool_indices;
-  const size_t lds = topk_lds_bytes(p.max_cand, p2);
-  // Raise the dynamic LDS limit to the full 160 KB once per device (not a stream
-  // operation, so it is done before any graph capture reaches here).
-  static std::mutex mu;
-  static uint64_t done_mask = 0;
-  int device = 0;
-  hipError_t e = hipGetDevice(&device);
-  if (e != hipSuccess) return e;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (device >= 64 || !(done_mask >> device & 1)) {
-      e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      if (device < 64) done_mask |= 1ull << device;
-    }
-  }
-  hipLaunchKernelGGL(topk_kernel, dim3(p.T), dim3(kNT), lds, st, a);
-  return hipGetLastError();
+  const int mc = p.max_cand;
+  const size_t lds = topk_lds_bytes(p.max_cand, p.topk);
+  if (mc <= 256) return launch_cfg<256, 1>(a, lds, st);
+  if (mc <= 512) return launch_cfg<256, 2>(a, lds, st);
+  if (mc <= 1024) return launch_cfg<256, 4>(a, lds, st);
+  if (mc <= 2048) return launch_cfg<256, 8>(a, lds, st);
+  if (mc <= 4096) return launch_cfg<256, 16>(a, lds, st);
+  if (mc <= 8192) return launch_cfg<512, 16>(a, lds, st);
+  if (mc <= 16384) return launch_cfg<1024, 16>(a, lds, st);
+  return launch_cfg<1024, 32>(a, lds, st);
 }
 
 }  // namespace dsa

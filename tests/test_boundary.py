@@ -64,7 +64,7 @@ def test_score_topk_validation(lib):
     assert _score(lib, prec=1, q_scale=None) == 1
     assert _score(lib, q_op=FAKE + 8) == 1                  # misaligned operand
     assert _score(lib, max_seqlen=1 << 17) == 2             # more candidates than the LDS selection holds
-    assert _score(lib, topk=4096, max_seqlen=32768) == 2
+    assert _score(lib, topk=32768, max_seqlen=32768) == 2   # selection buffer beyond LDS
     assert _score(lib, wsb=10) == 3                         # everything valid but the workspace
     assert b"workspace" in lib.dsa_last_error()
     assert _score(lib, T=0) == 0                            # empty problem: nothing to do
