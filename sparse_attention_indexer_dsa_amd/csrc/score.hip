@@ -48,6 +48,12 @@ struct ScoreArgs {
   int ntiles;                    // query tiles per document (ceil(max_seqlen / tokens per workgroup))
 };
 
+__device__ __forceinline__ float relu(float x) {
+  // max(x, 0) on the bit pattern: negative values (sign bit set, -0 included) become +0;
+  // one integer max, without the quieting step a float max needs in IEEE mode
+  return u2f((uint32_t)max((int)f2u(x), 0));
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   // lanes l and l^32 hold the two halves of the rows of one column: add them
   auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
@@ -65,8 +71,9 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
   constexpr int TQ = 4 * TPW;                    // tokens per workgroup
   constexpr int NSB = D / 32;                    // 32-element scale blocks per row
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kNK * ROWB];
-  __shared__ uint8_t ks_lds[kFP8 ? kNK * NSB : 1];
+  constexpr int NSBL = PREC == kPrecMXFP8 ? NSB : 1;   // key scales per LDS row
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kNK * ROWB];
+  __shared__ uint8_t ks_lds[2][kFP8 ? kNK * NSBL : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,37 +146,59 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     const int u = ut0 + j;
     cand_tok[j] = (j < TPW && u < L) ? min((u + 1) / kp, a.max_cand) : 0;
   }
+  // score row of the token this lane writes (H = 64: one token; H = 32 / 16: see below)
+  float* srow = a.scores + (long long)(lo + ut0) * a.stride + col;
 
-  const int n_tiles = (n_keys + kNK - 1) / kNK;
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int c0 = kt * kNK;
-    __syncthreads();
-    // ---- stage the key tile (zero rows past the candidates or the key array)
-    constexpr int CH = RB / 16;                  // 16-byte chunks per key row
+  // ---- key-tile staging: each thread moves NCH fixed 16-byte chunks of every tile; the
+  //      pointers advance by one tile per step and rows past the candidates (or the key
+  //      array) are staged as zeros
+  constexpr int CH = RB / 16;                    // 16-byte chunks per key row
+  constexpr int NCH = (kNK * CH + kThreads - 1) / kThreads;
+  const int lim = (int)min((long long)n_keys, (long long)a.S - kbase);   // stageable rows
+  const uint8_t* gptr[NCH];
+  int srow_of[NCH], lds_off[NCH];
 #pragma unroll
-    for (int it = 0; it < (kNK * CH + kThreads - 1) / kThreads; ++it) {
-      const int ch = it * kThreads + tid;
-      if (ch < kNK * CH) {
-        const int row = ch / CH, cc = ch % CH;
-        const int c = c0 + row;
-        const long long krow = (long long)kbase + c;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (c < n_keys && krow < a.S)
-          v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.k_op) + krow * RB + cc * 16);
-        *reinterpret_cast<uint4*>(k_lds + row * ROWB + cc * 16) = v;
-      }
+  for (int it = 0; it < NCH; ++it) {
+    const int ch = it * kThreads + tid;
+    const int row = ch / CH, cc = ch % CH;
+    srow_of[it] = ch < kNK * CH ? row : 1 << 30;
+    lds_off[it] = row * ROWB + cc * 16;
+    gptr[it] = reinterpret_cast<const uint8_t*>(a.k_op) + ((long long)kbase + row) * RB + cc * 16;
+  }
+  // scales: thread i < kNK * NSBL stages scale byte i of the tile
+  const int sc_row = tid / NSBL;
+  const bool sc_thread = kFP8 && tid < kNK * NSBL;
+  const uint8_t* sptr = kFP8 ? a.k_scale + ((long long)kbase + sc_row) * NSBL + tid % NSBL : nullptr;
+
+  uint4 stage[NCH];
+  uint8_t sstage = 127;
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      stage[it] = make_uint4(0, 0, 0, 0);
+      if (c0 + srow_of[it] < lim) stage[it] = *reinterpret_cast<const uint4*>(gptr[it] + (long long)c0 * RB);
     }
     if (kFP8) {
-      for (int i = tid; i < kNK * NSB; i += kThreads) {
-        const int row = i / NSB, blk = i % NSB;
-        const int c = c0 + row;
-        const long long krow = (long long)kbase + c;
-        uint8_t s = 127;
-        if (c < n_keys && krow < a.S) s = PREC == kPrecFP8 ? a.k_scale[krow] : a.k_scale[krow * NSB + blk];
-        ks_lds[i] = s;
-      }
+      sstage = 127;
+      if (sc_thread && c0 + sc_row < lim) sstage = sptr[(long long)c0 * NSBL];
     }
-    __syncthreads();
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < NCH; ++it)
+      if (srow_of[it] < kNK) *reinterpret_cast<uint4*>(&k_lds[buf][lds_off[it]]) = stage[it];
+    if (kFP8 && sc_thread) ks_lds[buf][tid] = sstage;
+  };
+
+  const int n_tiles = (n_keys + kNK - 1) / kNK;
+  fetch(0);
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int c0 = kt * kNK;
+    const int buf = kt & 1;
+    put(buf);
+    __syncthreads();                             // one barrier per tile: buffers alternate
+    if (kt + 1 < n_tiles) fetch(c0 + kNK);       // next tile's loads overlap this tile's math
+    const uint8_t* kl = k_lds[buf];
 
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -182,19 +211,19 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         if (kFP8) {
-          const uint8_t* src = k_lds + krow_l * ROWB + kk * 64 + 16 * hl;
+          const uint8_t* src = kl + krow_l * ROWB + kk * 64 + 16 * hl;
           uint4 v0 = *reinterpret_cast<const uint4*>(src);
           uint4 v1 = *reinterpret_cast<const uint4*>(src + 32);
           i32x8 bop;
           bop[0] = v0.x; bop[1] = v0.y; bop[2] = v0.z; bop[3] = v0.w;
           bop[4] = v1.x; bop[5] = v1.y; bop[6] = v1.z; bop[7] = v1.w;
-          const int bsc = ks_lds[krow_l * NSB + 2 * kk + hl];
+          const int bsc = PREC == kPrecFP8 ? ks_lds[buf][krow_l] : ks_lds[buf][krow_l * NSBL + 2 * kk + hl];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 *reinterpret_cast<const i32x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0, asc[rb][kk], 0, bsc);
         } else {
-          uint4 v = *reinterpret_cast<const uint4*>(k_lds + krow_l * ROWB + kk * 32 + 16 * hl);
+          uint4 v = *reinterpret_cast<const uint4*>(kl + krow_l * ROWB + kk * 32 + 16 * hl);
           bf16x8 bop = *reinterpret_cast<bf16x8*>(&v);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
@@ -210,31 +239,30 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), s);
+          for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), s);
         s = pair_sum(s) * a.sm_scale;
-        if (hl == 0 && c < cand_tok[0])
-          a.scores[(long long)(lo + ut0) * a.stride + c] = s;
+        if (hl == 0 && c < cand_tok[0]) srow[c0 + nb * 32] = s;
       } else if (H == 32) {
         float s[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           float v = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) v = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), v);
+          for (int i = 0; i < 16; ++i) v = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v);
           s[rb] = pair_sum(v) * a.sm_scale;
         }
         // lanes 0-31 write token 0, lanes 32-63 token 1
         const int ct = hl ? cand_tok[1] : cand_tok[0];
-        if (c < ct) a.scores[(long long)(lo + ut0 + hl) * a.stride + c] = hl ? s[1] : s[0];
+        if (c < ct) srow[(long long)hl * a.stride + c0 + nb * 32] = hl ? s[1] : s[0];
       } else {                                   // H == 16: rows 0-15 / 16-31 of a block are two tokens
         float s[4];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v0 = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), v0);
+          for (int i = 0; i < 8; ++i) v0 = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v0);
 #pragma unroll
-          for (int i = 8; i < 16; ++i) v1 = __builtin_fmaf(wl[rb][i], fmaxf(acc[rb][i], 0.f), v1);
+          for (int i = 8; i < 16; ++i) v1 = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v1);
           s[2 * rb] = pair_sum(v0) * a.sm_scale;
           s[2 * rb + 1] = pair_sum(v1) * a.sm_scale;
         }
@@ -243,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
           const int j = 2 * rb + hl;
           const float v = hl ? s[2 * rb + 1] : s[2 * rb];
           const int ct = hl ? cand_tok[2 * rb + 1] : cand_tok[2 * rb];
-          if (c < ct) a.scores[(long long)(lo + ut0 + j) * a.stride + c] = v;
+          if (c < ct) srow[(long long)j * a.stride + c0 + nb * 32] = v;
         }
       }
     }
