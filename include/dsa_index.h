@@ -92,7 +92,7 @@ typedef enum { DSA_DTYPE_BF16 = 0, DSA_DTYPE_FP32 = 1 } dsa_dtype_t;
  *             with a pinned pairwise halving sum, rstd = 1/sqrt(var + ln_eps), each fp32
  *             operation rounded separately. Queries get no LayerNorm.
  *   rope_cos, rope_sin fp32 [rope_max_pos, rope_dim/2]: angle table, row = position inside
- *             the document. rope_dim = 0 => NoPE (tables unused, may be NULL).
+ *             the document, 16-byte aligned. rope_dim = 0 => NoPE (tables unused, may be NULL).
  *             RoPE rotates the last rope_dim dims: rotate-half pairs (j, j+rope_dim/2) when
  *             rope_interleaved = 0 (rope_dim % 32 == 0 required), adjacent pairs (2j, 2j+1)
  *             when 1 (rope_dim even). y1 = x1*c - x2*s, y2 = x2*c + x1*s, no fused
@@ -205,7 +205,8 @@ dsa_status_t dsa_index_score_topk(
  * >= max(1, max_seqlen) (kpool == 1) or max(1, max_seqlen/kpool) (kpool > 1), and
  * cand(t) = u+1 or floor((u+1)/kpool) for t at position u of its document; entry c is the
  * score of document-local candidate c. Other workspace bytes are left untouched. Arguments
- * and errors are as for dsa_index_score_topk.
+ * and errors are as for dsa_index_score_topk, except that topk is not used and the bound on
+ * candidates per row is 4194304 (2^22) instead of 32768 (DSA_ERR_UNSUPPORTED above it).
  */
 dsa_status_t dsa_index_score(
     const void* q_op, const uint8_t* q_scale,

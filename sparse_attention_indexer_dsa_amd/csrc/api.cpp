@@ -91,6 +91,8 @@ dsa_status_t dsa_index_preprocess(
     return fail(DSA_ERR_UNSUPPORTED, "rotate-half RoPE needs rope_dim %% 32 == 0 (got %d)", rope_dim);
   if (rope_dim > 0 && (!rope_cos || !rope_sin || rope_max_pos < 1))
     return fail(DSA_ERR_INVALID_ARGUMENT, "rope tables and rope_max_pos >= 1 required when rope_dim > 0");
+  if (rope_dim > 0 && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "rope tables must be 16-byte aligned");
   const bool fp8 = precision != DSA_PREC_BF16;
   if (q_in) {
     if (!q_op) return fail(DSA_ERR_INVALID_ARGUMENT, "q_op is NULL");
@@ -161,6 +163,9 @@ size_t dsa_index_workspace_size(int32_t T, int32_t H, int32_t D, int32_t num_seq
 
 namespace {
 
+// Per-document byte offsets into keys and score rows are 32-bit in the kernels.
+constexpr int kMaxCandidates = 1 << 22;
+
 // Validation shared by the scoring and selection entry points. Fills `p` on success.
 dsa_status_t check_geometry(int T, const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int kpool,
                             const int32_t* cu_pools, int topk, bool need_topk) {
@@ -172,6 +177,8 @@ dsa_status_t check_geometry(int T, const int32_t* cu_seqlens, int num_seqs, int 
   if (max_seqlen < 0 || (T > 0 && max_seqlen < 1))
     return fail(DSA_ERR_INVALID_ARGUMENT, "max_seqlen=%d must be >= 1", max_seqlen);
   const int max_cand = max_candidates(max_seqlen, kpool);
+  if (max_cand > kMaxCandidates)
+    return fail(DSA_ERR_UNSUPPORTED, "%d candidates per row exceed the supported %d", max_cand, kMaxCandidates);
   if (need_topk) {
     if (max_cand > dsa::kTopkMaxCand)
       return fail(DSA_ERR_UNSUPPORTED, "%d candidates per row exceed the supported %d", max_cand, dsa::kTopkMaxCand);

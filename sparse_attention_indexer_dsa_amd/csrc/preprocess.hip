@@ -37,21 +37,41 @@ __device__ __forceinline__ int token_position(const int32_t* cu, int B, int T, i
 
 // ------------------------------------------------------------------ queries
 
-template <int D, bool IN_BF16, int PREC>
-__global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
-  constexpr int G = D / 8;                       // lanes per vector
-  constexpr int VPB = 256 / G;                   // vectors per block
-  const int g = threadIdx.x % G;
-  const long long v = (long long)blockIdx.x * VPB + threadIdx.x / G;
-  const long long nvec = (long long)a.T * a.H;
-  const bool live = v < nvec;
-  const long long vv = live ? v : 0;
-  const int t = (int)(vv / a.H);
+// Max over lane groups of fp32 magnitudes (non-negative floats order like their bits):
+// 16 lanes = one DPP row, 8 lanes = half a row, 4 lanes = a quad.
+template <int N>
+__device__ __forceinline__ float group_amax(float a) {
+  uint32_t m = f2u(a);
+  if (N == 16) {
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x121, 0xf, 0xf, false));   // row_ror:1
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x122, 0xf, 0xf, false));   // row_ror:2
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x124, 0xf, 0xf, false));   // row_ror:4
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xf, 0xf, false));   // row_ror:8
+  } else {
+    if (N == 8) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  }
+  return u2f(m);
+}
 
-  float x[8];
+// Eight E4M3 codes of x * 2^-e (exact scaling; the codes are the round-to-nearest-even
+// ones, which the gfx950 conversion produces bit for bit for |values| <= 448).
+__device__ __forceinline__ uint2 e4m3_pack8(const float (&x)[8], int e) {
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * h], -e), ldexpf(x[4 * h + 1], -e), 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * h + 2], -e), ldexpf(x[4 * h + 3], -e), v, true);
+    w[h] = (uint32_t)v;
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void* base, long long off, float (&x)[8]) {
   if (IN_BF16) {
-    uint4 raw = live ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q_in) + vv * D + 8 * g)
-                     : make_uint4(0, 0, 0, 0);
+    const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -59,11 +79,32 @@ __global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
       x[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q_in) + vv * D + 8 * g);
-    float4 lo = live ? p[0] : make_float4(0, 0, 0, 0), hi = live ? p[1] : make_float4(0, 0, 0, 0);
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    const float4 lo = p[0], hi = p[1];
     x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w; x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
   }
-  if (!a.rope_fp32) {
+}
+
+__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
+  const float4 lo = reinterpret_cast<const float4*>(p)[0], hi = reinterpret_cast<const float4*>(p)[1];
+  x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w; x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+}
+
+// One (t, h) query vector per group of D/8 lanes; lane g owns elements 8g .. 8g+7.
+template <int D, bool IN_BF16, int PREC>
+__device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
+  constexpr int G = D / 8;                       // lanes per vector
+  constexpr int VPB = 256 / G;                   // vectors per block
+  const int g = threadIdx.x % G;
+  const long long v = (long long)block * VPB + threadIdx.x / G;
+  const long long nvec = (long long)a.T * a.H;
+  if (v >= nvec) return;                         // no cross-lane work below spans vectors
+  const int t = (int)(v / a.H);
+  const long long base = v * D + 8 * g;
+
+  float x[8];
+  load8<IN_BF16>(a.q_in, base, x);
+  if (!IN_BF16 && !a.rope_fp32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = bf16_round(x[j]);
   }
@@ -86,24 +127,22 @@ __global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
           x[j + 1] = x2 * c + x1 * s;
         }
       }
-    } else {
-      // partner lane holds the other half of each rotated pair in the same slot
-      const int lanes_half = half / 8;
-      const bool in_rope = 8 * g >= rs;
+    } else if (8 * g >= rs) {
+      // rotate-half: the partner elements are half a rotation away in the same vector;
+      // they are read from memory (the partner lane's cache lines) rather than shuffled
       const bool first = 8 * g < rs + half;
-      const int src_g = !in_rope ? g : (first ? g + lanes_half : g - lanes_half);
-      const int src = (threadIdx.x & 63) - g + src_g;
       float p[8];
+      load8<IN_BF16>(a.q_in, base + (first ? half : -half), p);
+      if (!IN_BF16 && !a.rope_fp32) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = __shfl(x[j], src, 64);
-      if (in_rope) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = 8 * g + j - rs - (first ? 0 : half);
-          const float c = crow[col], s = srow[col];
-          x[j] = first ? (x[j] * c - p[j] * s) : (x[j] * c + p[j] * s);
-        }
+        for (int j = 0; j < 8; ++j) p[j] = bf16_round(p[j]);
       }
+      const int col = 8 * g - rs - (first ? 0 : half);
+      float c[8], sn[8];
+      load8f(crow + col, c);
+      load8f(srow + col, sn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = first ? (x[j] * c[j] - p[j] * sn[j]) : (x[j] * c[j] + p[j] * sn[j]);
     }
     if (!a.rope_fp32) {
 #pragma unroll
@@ -111,8 +150,8 @@ __global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
     }
   }
 
-  if (a.q_f32 && live) {
-    float4* o = reinterpret_cast<float4*>(a.q_f32 + vv * D + 8 * g);
+  if (a.q_f32) {
+    float4* o = reinterpret_cast<float4*>(a.q_f32 + base);
     o[0] = make_float4(x[0], x[1], x[2], x[3]);
     o[1] = make_float4(x[4], x[5], x[6], x[7]);
   }
@@ -122,29 +161,19 @@ __global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       w[j] = (uint32_t)f32_to_bf16_rne(x[2 * j]) | ((uint32_t)f32_to_bf16_rne(x[2 * j + 1]) << 16);
-    if (live)
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op) + vv * D + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op) + base) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
-    // per-vector: reduce over the G lanes; per-32: over 4 lanes
-    constexpr int RED = (PREC == kPrecFP8) ? G : 4;
-#pragma unroll
-    for (int off = 1; off < RED; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    // per-vector scale: all G lanes of the vector; per-32 scale: the 4 lanes of the block
+    amax = group_amax<(PREC == kPrecFP8) ? G : 4>(amax);
     const int e = ue8m0_exponent(amax);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= e4m3_encode(ldexpf(x[j], -e)) << (8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= e4m3_encode(ldexpf(x[4 + j], -e)) << (8 * j);
-    if (live) {
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.q_op) + vv * D + 8 * g) = make_uint2(lo, hi);
-      if (PREC == kPrecFP8) {
-        if (g == 0) a.q_scale[vv] = (uint8_t)(e + 127);
-      } else {
-        if ((g & 3) == 0) a.q_scale[vv * (D / 32) + g / 4] = (uint8_t)(e + 127);
-      }
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.q_op) + base) = e4m3_pack8(x, e);
+    if (PREC == kPrecFP8) {
+      if (g == 0) a.q_scale[v] = (uint8_t)(e + 127);
+    } else {
+      if ((g & 3) == 0) a.q_scale[v * (D / 32) + g / 4] = (uint8_t)(e + 127);
     }
   }
 }
@@ -152,12 +181,12 @@ __global__ __launch_bounds__(256) void preprocess_q_kernel(PreArgs a) {
 // ------------------------------------------------------------------ keys
 
 template <int D, bool IN_BF16, int PREC>
-__global__ __launch_bounds__(256) void preprocess_k_kernel(PreArgs a) {
+__device__ __forceinline__ void preprocess_k(const PreArgs& a, int block) {
   constexpr int V = D / 16;                      // elements per lane
   const int g = threadIdx.x & 15;
   const int lane = threadIdx.x & 63;
   const int gbase = lane - g;
-  const int s_raw = blockIdx.x * 16 + threadIdx.x / 16;
+  const int s_raw = block * 16 + threadIdx.x / 16;
   const bool live = s_raw < a.S;
   const int s = live ? s_raw : 0;
 
@@ -294,22 +323,21 @@ __global__ __launch_bounds__(256) void preprocess_k_kernel(PreArgs a) {
   }
 }
 
+// One launch: the first blocks preprocess keys (16 tokens each), the rest queries.
+template <int D, bool IN_BF16, int PREC>
+__global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a, int k_blocks) {
+  if ((int)blockIdx.x < k_blocks) preprocess_k<D, IN_BF16, PREC>(a, blockIdx.x);
+  else preprocess_q<D, IN_BF16, PREC>(a, blockIdx.x - k_blocks);
+}
+
 template <int D, bool IN_BF16, int PREC>
 hipError_t launch_pre(const PreArgs& a, hipStream_t st) {
-  if (a.q_in && a.T > 0) {
-    const long long nvec = (long long)a.T * a.H;
-    const long long blocks = (nvec + (256 / (D / 8)) - 1) / (256 / (D / 8));
-    hipLaunchKernelGGL((preprocess_q_kernel<D, IN_BF16, PREC>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.k_in && a.S > 0) {
-    const int blocks = (a.S + 15) / 16;
-    hipLaunchKernelGGL((preprocess_k_kernel<D, IN_BF16, PREC>), dim3(blocks), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const long long q_blocks = (a.q_in && a.T > 0) ? ((long long)a.T * a.H + (256 / (D / 8)) - 1) / (256 / (D / 8)) : 0;
+  const long long k_blocks = (a.k_in && a.S > 0) ? (a.S + 15) / 16 : 0;
+  if (q_blocks + k_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((preprocess_kernel<D, IN_BF16, PREC>), dim3((unsigned)(q_blocks + k_blocks)), dim3(256), 0, st,
+                     a, (int)k_blocks);
+  return hipGetLastError();
 }
 
 template <int D, bool IN_BF16>

@@ -36,6 +36,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kNK = 64;          // keys per LDS tile
 constexpr int kThreads = 256;
+constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: raw 32-bit data format
 
 struct ScoreArgs {
   const void* q_op; const uint8_t* q_scale;
@@ -47,6 +48,16 @@ struct ScoreArgs {
   float* scores; int stride; int max_cand;
   int ntiles;                    // query tiles per document (ceil(max_seqlen / tokens per workgroup))
 };
+
+// Buffer descriptor over `bytes` bytes at `base` (both wave-uniform; read from lane 0 so the
+// descriptor lives in scalar registers). Loads past `bytes` return zeros, stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t plo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t phi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)phi << 32) | plo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
 
 __device__ __forceinline__ float relu(float x) {
   // max(x, 0) on the bit pattern: negative values (sign bit set, -0 included) become +0;
@@ -146,136 +157,193 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     const int u = ut0 + j;
     cand_tok[j] = (j < TPW && u < L) ? min((u + 1) / kp, a.max_cand) : 0;
   }
-  // score row of the token this lane writes (H = 64: one token; H = 32 / 16: see below)
-  float* srow = a.scores + (long long)(lo + ut0) * a.stride + col;
+  // score rows of this wave's tokens, as a buffer: lanes that write nothing (masked
+  // candidates, duplicate lanes) store to an offset past its end, which the hardware drops
+  const __amdgpu_buffer_rsrc_t out_r =
+      make_rsrc(a.scores + (long long)(lo + ut0) * a.stride, TPW * a.stride * 4);
+  constexpr uint32_t kDrop = 0xFFFFFFF0u;
 
-  // ---- key-tile staging: each thread moves NCH fixed 16-byte chunks of every tile; the
-  //      pointers advance by one tile per step and rows past the candidates (or the key
-  //      array) are staged as zeros
+  // ---- key-tile staging through buffer loads: the buffer covers the stageable rows of this
+  //      document (candidates that exist in the key array), so rows past them read as zeros
+  //      without branches. Each thread moves NCH fixed 16-byte chunks of every tile; only
+  //      the descriptor's base (a scalar) advances from tile to tile.
   constexpr int CH = RB / 16;                    // 16-byte chunks per key row
-  constexpr int NCH = (kNK * CH + kThreads - 1) / kThreads;
-  const int lim = (int)min((long long)n_keys, (long long)a.S - kbase);   // stageable rows
-  const uint8_t* gptr[NCH];
-  int srow_of[NCH], lds_off[NCH];
+  static_assert((kNK * CH) % kThreads == 0, "tile chunks must divide over the workgroup");
+  constexpr int NCH = kNK * CH / kThreads;
+  constexpr int NSC = kNK * NSBL;                // scale bytes per tile
+  const int lim = (int)max(0LL, min((long long)n_keys, (long long)a.S - kbase));   // stageable rows
+  const uint8_t* kdoc = reinterpret_cast<const uint8_t*>(a.k_op) + (long long)kbase * RB;
+  const uint8_t* sdoc = kFP8 ? a.k_scale + (long long)kbase * NSBL : nullptr;
+  int goff[NCH], lds_off[NCH];
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
     const int ch = it * kThreads + tid;
     const int row = ch / CH, cc = ch % CH;
-    srow_of[it] = ch < kNK * CH ? row : 1 << 30;
+    goff[it] = row * RB + cc * 16;
     lds_off[it] = row * ROWB + cc * 16;
-    gptr[it] = reinterpret_cast<const uint8_t*>(a.k_op) + ((long long)kbase + row) * RB + cc * 16;
   }
-  // scales: thread i < kNK * NSBL stages scale byte i of the tile
-  const int sc_row = tid / NSBL;
-  const bool sc_thread = kFP8 && tid < kNK * NSBL;
-  const uint8_t* sptr = kFP8 ? a.k_scale + ((long long)kbase + sc_row) * NSBL + tid % NSBL : nullptr;
+  const int sc_i = tid % NSC;                    // scale byte this thread stages (duplicates agree)
 
-  uint4 stage[NCH];
-  uint8_t sstage = 127;
-  auto fetch = [&](int c0) {
+  struct Stage { uint4 v[NCH]; uint32_t s; };
+  auto fetch = [&](Stage& st, int c0) {
+    const int rem = max(0, lim - c0);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kdoc + (long long)c0 * RB, rem * RB);
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      stage[it] = make_uint4(0, 0, 0, 0);
-      if (c0 + srow_of[it] < lim) stage[it] = *reinterpret_cast<const uint4*>(gptr[it] + (long long)c0 * RB);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[it], 0, 0);
+      st.v[it] = make_uint4(v[0], v[1], v[2], v[3]);
     }
+    st.s = 0;
     if (kFP8) {
-      sstage = 127;
-      if (sc_thread && c0 + sc_row < lim) sstage = sptr[(long long)c0 * NSBL];
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(sdoc + (long long)c0 * NSBL, rem * NSBL);
+      st.s = __builtin_amdgcn_raw_buffer_load_b8(sr, sc_i, 0, 0);
     }
   };
-  auto put = [&](int buf) {
+  auto put = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int it = 0; it < NCH; ++it)
-      if (srow_of[it] < kNK) *reinterpret_cast<uint4*>(&k_lds[buf][lds_off[it]]) = stage[it];
-    if (kFP8 && sc_thread) ks_lds[buf][tid] = sstage;
+    for (int it = 0; it < NCH; ++it) *reinterpret_cast<uint4*>(&k_lds[buf][lds_off[it]]) = st.v[it];
+    if (kFP8) ks_lds[buf][sc_i] = (uint8_t)st.s;
   };
 
-  const int n_tiles = (n_keys + kNK - 1) / kNK;
-  fetch(0);
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int c0 = kt * kNK;
-    const int buf = kt & 1;
-    put(buf);
-    __syncthreads();                             // one barrier per tile: buffers alternate
-    if (kt + 1 < n_tiles) fetch(c0 + kNK);       // next tile's loads overlap this tile's math
+  // ---- one 32-key column block: q.k on MFMA into acc
+  typedef f32x16 Acc[2];
+  auto mma = [&](int buf, int nb, Acc& acc) {
     const uint8_t* kl = k_lds[buf];
-
+    const int krow_l = nb * 32 + col;            // key (LDS row) of this lane's B operand / C column
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int krow_l = nb * 32 + col;          // key (LDS row) of this lane's B operand / C column
-      f32x16 acc[2];
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kFP8) {
+        const uint8_t* src = kl + krow_l * ROWB + kk * 64 + 16 * hl;
+        uint4 v0 = *reinterpret_cast<const uint4*>(src);
+        uint4 v1 = *reinterpret_cast<const uint4*>(src + 32);
+        i32x8 bop;
+        bop[0] = v0.x; bop[1] = v0.y; bop[2] = v0.z; bop[3] = v0.w;
+        bop[4] = v1.x; bop[5] = v1.y; bop[6] = v1.z; bop[7] = v1.w;
+        const int bsc = PREC == kPrecFP8 ? ks_lds[buf][krow_l] : ks_lds[buf][krow_l * NSBL + 2 * kk + hl];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              *reinterpret_cast<const i32x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0, asc[rb][kk], 0, bsc);
+      } else {
+        uint4 v = *reinterpret_cast<const uint4*>(kl + krow_l * ROWB + kk * 32 + 16 * hl);
+        bf16x8 bop = *reinterpret_cast<bf16x8*>(&v);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- ReLU, weights and head sum of one column block (first candidate cb) in registers
+  auto epilogue = [&](const Acc& acc, int cb) {
+    const int c = cb + col;                      // candidate index (document-local)
+    if (H == 64) {
+      float s = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), s);
+      s = pair_sum(s) * a.sm_scale;
+      const uint32_t off = (hl == 0 && (uint32_t)c < (uint32_t)cand_tok[0]) ? (uint32_t)c * 4u : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(f2u(s), out_r, off, 0, 0);
+    } else if (H == 32) {
+      float s[2];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        if (kFP8) {
-          const uint8_t* src = kl + krow_l * ROWB + kk * 64 + 16 * hl;
-          uint4 v0 = *reinterpret_cast<const uint4*>(src);
-          uint4 v1 = *reinterpret_cast<const uint4*>(src + 32);
-          i32x8 bop;
-          bop[0] = v0.x; bop[1] = v0.y; bop[2] = v0.z; bop[3] = v0.w;
-          bop[4] = v1.x; bop[5] = v1.y; bop[6] = v1.z; bop[7] = v1.w;
-          const int bsc = PREC == kPrecFP8 ? ks_lds[buf][krow_l] : ks_lds[buf][krow_l * NSBL + 2 * kk + hl];
+      for (int rb = 0; rb < 2; ++rb) {
+        float v = 0.f;
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                *reinterpret_cast<const i32x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0, asc[rb][kk], 0, bsc);
-        } else {
-          uint4 v = *reinterpret_cast<const uint4*>(kl + krow_l * ROWB + kk * 32 + 16 * hl);
-          bf16x8 bop = *reinterpret_cast<bf16x8*>(&v);
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *reinterpret_cast<const bf16x8*>(&aop[rb][kk]), bop, acc[rb], 0, 0, 0);
-        }
+        for (int i = 0; i < 16; ++i) v = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v);
+        s[rb] = pair_sum(v) * a.sm_scale;
       }
-
-      // ---- ReLU, weights and head sum in registers
-      const int c = c0 + nb * 32 + col;          // candidate index (document-local)
-      if (H == 64) {
-        float s = 0.f;
+      // lanes 0-31 write token 0, lanes 32-63 token 1
+      const int ct = hl ? cand_tok[1] : cand_tok[0];
+      const uint32_t off = (uint32_t)c < (uint32_t)ct ? (uint32_t)(hl * a.stride + c) * 4u : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(f2u(hl ? s[1] : s[0]), out_r, off, 0, 0);
+    } else {                                     // H == 16: rows 0-15 / 16-31 of a block are two tokens
+      float s[4];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb) {
+        float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), s);
-        s = pair_sum(s) * a.sm_scale;
-        if (hl == 0 && c < cand_tok[0]) srow[c0 + nb * 32] = s;
-      } else if (H == 32) {
-        float s[2];
+        for (int i = 0; i < 8; ++i) v0 = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v0);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float v = 0.f;
+        for (int i = 8; i < 16; ++i) v1 = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v1);
+        s[2 * rb] = pair_sum(v0) * a.sm_scale;
+        s[2 * rb + 1] = pair_sum(v1) * a.sm_scale;
+      }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) v = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v);
-          s[rb] = pair_sum(v) * a.sm_scale;
-        }
-        // lanes 0-31 write token 0, lanes 32-63 token 1
-        const int ct = hl ? cand_tok[1] : cand_tok[0];
-        if (c < ct) srow[(long long)hl * a.stride + c0 + nb * 32] = hl ? s[1] : s[0];
-      } else {                                   // H == 16: rows 0-15 / 16-31 of a block are two tokens
-        float s[4];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v0 = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v0);
-#pragma unroll
-          for (int i = 8; i < 16; ++i) v1 = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), v1);
-          s[2 * rb] = pair_sum(v0) * a.sm_scale;
-          s[2 * rb + 1] = pair_sum(v1) * a.sm_scale;
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int j = 2 * rb + hl;
-          const float v = hl ? s[2 * rb + 1] : s[2 * rb];
-          const int ct = hl ? cand_tok[2 * rb + 1] : cand_tok[2 * rb];
-          if (c < ct) srow[(long long)j * a.stride + c0 + nb * 32] = v;
-        }
+      for (int rb = 0; rb < 2; ++rb) {
+        const int j = 2 * rb + hl;
+        const float v = hl ? s[2 * rb + 1] : s[2 * rb];
+        const int ct = hl ? cand_tok[2 * rb + 1] : cand_tok[2 * rb];
+        const uint32_t off = (uint32_t)c < (uint32_t)ct ? (uint32_t)(j * a.stride + c) * 4u : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b32(f2u(v), out_r, off, 0, 0);
       }
     }
+  };
+
+  // ---- sweep. Tiles alternate between two LDS buffers and two register stages: while
+  //      tile kt is multiplied out of one buffer, tile kt + 1 waits in registers for the other
+  //      buffer and tile kt + 2 is in flight, so a load has two tiles of work to land. Each
+  //      column block's epilogue runs while the next block's MFMAs execute (the first call
+  //      of a workgroup stores nothing: its candidates are negative). One barrier per tile.
+  const int n_tiles = (n_keys + kNK - 1) / kNK;
+  if (n_tiles == 0) return;
+  Acc acc0, acc1;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc1[rb][i] = 0.f;
+  auto compute = [&](int buf, int c0) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma(buf, 0, acc0);
+    epilogue(acc1, c0 - 32);
+    mma(buf, 1, acc1);
+    epilogue(acc0, c0);
+    // Issue order: a wave issues in order and an MFMA occupies the matrix pipe for many
+    // cycles, so each MFMA is followed by a share of the other block's epilogue rather
+    // than the MFMAs of a block being issued back to back.
+    constexpr int NM = 2 * (kFP8 ? KSTEPS : KSTEPS);      // MFMAs per column block
+    constexpr int NR = kFP8 ? 2 * KSTEPS + 1 : KSTEPS;    // LDS reads per column block
+    constexpr int VPM = 72 / NM;                          // epilogue VALU per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  Stage sa, sb;
+  fetch(sa, 0);
+  fetch(sb, kNK);
+  put(sa, 0);
+  __syncthreads();
+  fetch(sa, 2 * kNK);
+  int kt = 0;
+  for (; kt + 1 < n_tiles; kt += 2) {            // buffer 0 holds tile kt, sb tile kt+1, sa tile kt+2
+    compute(0, kt * kNK);
+    put(sb, 1);
+    __syncthreads();
+    fetch(sb, (kt + 3) * kNK);
+    compute(1, (kt + 1) * kNK);
+    put(sa, 0);
+    __syncthreads();
+    fetch(sa, (kt + 4) * kNK);
   }
+  if (kt < n_tiles) compute(0, kt * kNK);        // odd tile count: the last tile is in buffer 0
+  epilogue(acc1, n_tiles * kNK - 32);
 }
 
 template <int H, int D, int PREC>

@@ -48,9 +48,19 @@ def host(t):
     return t.cpu().numpy()
 
 
+def dev_in(a):
+    """Device tensor of an input held as bf16 bits (uint16) or as float32 values."""
+    return dev(a) if a.dtype == np.float32 else dev_bf16(a)
+
+
+def in_f32(a):
+    """fp32 values of an input held as bf16 bits (uint16) or as float32 values."""
+    return np.asarray(a, np.float32) if a.dtype == np.float32 else gen.bf16_bits_to_f32(a)
+
+
 def gpu_inputs(inp):
     """Device tensors of a generated problem."""
-    d = dict(q=dev_bf16(inp["q"]), k=dev_bf16(inp["k"]), w=dev(inp["w"]), cu=dev(inp["cu_seqlens"]))
+    d = dict(q=dev_in(inp["q"]), k=dev_in(inp["k"]), w=dev(inp["w"]), cu=dev(inp["cu_seqlens"]))
     for name in ("gamma", "beta", "cos", "sin", "bias"):
         if name in inp:
             d[name] = dev(inp[name])
@@ -129,8 +139,8 @@ def fetch_rows(gd, rows, T, max_seqlen, kp):
 def oracle_operands(inp, cfg):
     """Scoring operands (and pooled keys) computed by the oracle from the same inputs."""
     prec, kp = cfg["precision"], cfg.get("kpool", 1)
-    q32 = gen.bf16_bits_to_f32(inp["q"])
-    k32 = gen.bf16_bits_to_f32(inp["k"])
+    q32 = in_f32(inp["q"])
+    k32 = in_f32(inp["k"])
     if cfg.get("preprocess"):
         qc, kc = orc.preprocess(q32, k32, inp["cu_seqlens"],
                                 gamma=inp.get("gamma") if cfg.get("layernorm") else None,
@@ -270,8 +280,8 @@ def oracle_operands_rows(inp, cfg, rows, keys=True):
     """Oracle operands of the sampled query rows (dict t -> values) and, if ``keys``, of all keys."""
     prec, kp = cfg["precision"], cfg.get("kpool", 1)
     rows = np.asarray(rows, np.int64)
-    q32 = gen.bf16_bits_to_f32(inp["q"][rows])
-    k32 = gen.bf16_bits_to_f32(inp["k"]) if keys else None
+    q32 = in_f32(inp["q"][rows])
+    k32 = in_f32(inp["k"]) if keys else None
     if cfg.get("preprocess"):
         qc, kc = orc.preprocess(q32, k32, inp["cu_seqlens"],
                                 gamma=inp.get("gamma") if cfg.get("layernorm") else None,

@@ -70,6 +70,16 @@ def test_score_topk_validation(lib):
     assert _score(lib, T=0) == 0                            # empty problem: nothing to do
 
 
+def test_score_only_candidate_bound(lib):
+    def score(max_seqlen, kpool=1):
+        return lib.dsa_index_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 128, FAKE, 1, max_seqlen, kpool,
+                                   FAKE if kpool > 1 else None, 1.0, 0, FAKE, 10, None)
+    assert score(1 << 23) == 2                  # byte offsets inside a document would pass 32 bits
+    assert b"candidates per row" in lib.dsa_last_error()
+    assert score(1 << 23, kpool=2) == 3         # 2^22 pools: only the workspace is missing
+    assert score(1 << 20) == 3
+
+
 def _pre(lib, **kw):
     a = dict(q=FAKE, k=FAKE, dt=0, T=64, S=64, H=64, D=128, cu=FAKE, B=1, g=None, b=None, eps=1e-6, cos=None,
              sin=None, R=0, maxpos=0, inter=0, f32=0, prec=0, qo=FAKE, qs=FAKE, ko=FAKE, ks=FAKE, qf=None, kf=None)
@@ -87,6 +97,7 @@ def test_preprocess_validation(lib):
     assert _pre(lib, R=63, cos=FAKE, sin=FAKE, maxpos=10) == 2
     assert _pre(lib, R=48, cos=FAKE, sin=FAKE, maxpos=10) == 2   # rotate-half needs a multiple of 32
     assert _pre(lib, R=64, cos=None, sin=None, maxpos=10) == 1
+    assert _pre(lib, R=64, cos=FAKE + 4, sin=FAKE, maxpos=10) == 1     # tables must be 16-byte aligned
     assert _pre(lib, R=130, cos=FAKE, sin=FAKE, maxpos=10, inter=1) == 2
     assert _pre(lib, prec=1, qs=None) == 1
     assert _pre(lib, dt=9) == 1

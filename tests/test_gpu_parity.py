@@ -83,6 +83,26 @@ def test_preprocess_and_score(precision, rope_fp32, interleaved, HD):
 
 
 @pytest.mark.parametrize("precision", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("rope_fp32", [False, True])
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_preprocess_fp32_inputs(precision, rope_fp32, interleaved):
+    # fp32 inputs that bf16 cannot hold: the bf16 carrier rounding (rope_fp32 off) is visible
+    H, D = 64, 128
+    cfg = dict(precision=precision, preprocess=True, layernorm=True, rope_dim=64, rope_fp32=rope_fp32,
+               interleaved=interleaved)
+    inp = gen.small(61 + rope_fp32 + 2 * interleaved, [40, 0, 77], H, D, layernorm=True, rope_dim=64)
+    rng = np.random.default_rng(5)
+    inp["q"] = (rng.standard_normal(inp["q"].shape) * 3.0).astype(np.float32)
+    inp["k"] = (rng.standard_normal(inp["k"].shape) * 0.5 + 0.25).astype(np.float32)
+    g = parity.gpu_pipeline(inp, cfg, 16)
+    o = parity.oracle_operands(inp, cfg)
+    assert np.array_equal(g["q_op"].view(np.uint8), np.asarray(o["q_op"]).view(np.uint8))
+    assert np.array_equal(g["k_op"].view(np.uint8), np.asarray(o["k_op"]).view(np.uint8))
+    if precision != "bf16":
+        assert np.array_equal(g["q_scale"], o["q_scale"]) and np.array_equal(g["k_scale"], o["k_scale"])
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8", "mxfp8"])
 def test_quantize_only(precision):
     # no LayerNorm, no RoPE: bf16 inputs quantised for scoring
     cfg = dict(precision=precision, preprocess=True, layernorm=False, rope_dim=0)
