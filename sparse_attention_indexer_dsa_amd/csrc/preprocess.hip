@@ -6,8 +6,8 @@
 // the input and the output of RoPE are rounded to bf16 (the default path's materialised
 // BF16, Megatron-LM PR 8403, "What does this PR do?" and "Motivation").
 //
-// Layouts. Queries: one vector (t,h) of D elements per group of D/8 lanes, lane g holding
-// the 8 contiguous elements 8g..8g+7 (16-byte loads and stores). Keys: one token per
+// Layouts. Queries: one vector (t,h) of D elements per group of D/16 lanes, lane g holding
+// the 16 contiguous elements 16g .. 16g+15. Keys: one token per
 // group of 16 lanes, lane g holding elements g, g+16, g+32, ... so that the halving sum
 // a[i] += a[i+n] is in-lane for n >= 16 and a single shuffle for n = 8, 4, 2, 1.
 #include <hip/hip_runtime.h>
@@ -38,10 +38,11 @@ __device__ __forceinline__ int token_position(const int32_t* cu, int B, int T, i
 // ------------------------------------------------------------------ queries
 
 // Max over lane groups of fp32 magnitudes (non-negative floats order like their bits):
-// 16 lanes = one DPP row, 8 lanes = half a row, 4 lanes = a quad.
+// 16 lanes = one DPP row, 8 lanes = half a row, 4 lanes = a quad, 2 lanes = a pair.
 template <int N>
 __device__ __forceinline__ float group_amax(float a) {
   uint32_t m = f2u(a);
+  if (N == 1) return a;
   if (N == 16) {
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x121, 0xf, 0xf, false));   // row_ror:1
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x122, 0xf, 0xf, false));   // row_ror:2
@@ -50,75 +51,91 @@ __device__ __forceinline__ float group_amax(float a) {
   } else {
     if (N == 8) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xf, 0xf, false));  // row_half_mirror
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    if (N >= 4) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
   }
   return u2f(m);
 }
 
-// Eight E4M3 codes of x * 2^-e (exact scaling; the codes are the round-to-nearest-even
-// ones, which the gfx950 conversion produces bit for bit for |values| <= 448).
-__device__ __forceinline__ uint2 e4m3_pack8(const float (&x)[8], int e) {
-  uint32_t w[2];
+// E4M3 codes of x * 2^-e, four per word (exact scaling; the codes are the
+// round-to-nearest-even ones, which the gfx950 conversion produces bit for bit for
+// |values| <= 448).
+template <int N>
+__device__ __forceinline__ void e4m3_pack(const float (&x)[N], int e, uint32_t (&w)[N / 4]) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < N / 4; ++h) {
     int v = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * h], -e), ldexpf(x[4 * h + 1], -e), 0, false);
     v = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * h + 2], -e), ldexpf(x[4 * h + 3], -e), v, true);
     w[h] = (uint32_t)v;
   }
-  return make_uint2(w[0], w[1]);
 }
 
-template <bool IN_BF16>
-__device__ __forceinline__ void load8(const void* base, long long off, float (&x)[8]) {
+// N contiguous input elements (bf16 bits or fp32) at element offset `off`, widened to fp32.
+template <bool IN_BF16, int N>
+__device__ __forceinline__ void load_in(const void* base, long long off, float (&x)[N]) {
   if (IN_BF16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = u2f(w[j] << 16);
-      x[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+    for (int c = 0; c < N / 8; ++c) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off + 8 * c);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * c + 2 * j] = u2f(w[j] << 16);
+        x[8 * c + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+      }
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-    const float4 lo = p[0], hi = p[1];
-    x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w; x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off + 4 * c);
+      x[4 * c] = f.x; x[4 * c + 1] = f.y; x[4 * c + 2] = f.z; x[4 * c + 3] = f.w;
+    }
   }
 }
 
-__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
-  const float4 lo = reinterpret_cast<const float4*>(p)[0], hi = reinterpret_cast<const float4*>(p)[1];
-  x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w; x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+template <int N>
+__device__ __forceinline__ void load_f32(const float* p, float (&x)[N]) {
+#pragma unroll
+  for (int c = 0; c < N / 4; ++c) {
+    const float4 f = reinterpret_cast<const float4*>(p)[c];
+    x[4 * c] = f.x; x[4 * c + 1] = f.y; x[4 * c + 2] = f.z; x[4 * c + 3] = f.w;
+  }
 }
 
-// One (t, h) query vector per group of D/8 lanes; lane g owns elements 8g .. 8g+7.
-template <int D, bool IN_BF16, int PREC>
+// One (t, h) query vector per group of D/NE lanes; lane g owns elements NE*g .. NE*g+NE-1.
+// With rotate-half RoPE a lane's elements must rotate together: NE divides rope_dim/2.
+template <int D, bool IN_BF16, int PREC, int NE>
 __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
-  constexpr int G = D / 8;                       // lanes per vector
+  constexpr int G = D / NE;                      // lanes per vector
   constexpr int VPB = 256 / G;                   // vectors per block
   const int g = threadIdx.x % G;
   const long long v = (long long)block * VPB + threadIdx.x / G;
   const long long nvec = (long long)a.T * a.H;
   if (v >= nvec) return;                         // no cross-lane work below spans vectors
   const int t = (int)(v / a.H);
-  const long long base = v * D + 8 * g;
+  const long long base = v * D + NE * g;
+  const int e0 = NE * g;                         // first element of this lane
 
-  float x[8];
-  load8<IN_BF16>(a.q_in, base, x);
+  float x[NE];
+  load_in<IN_BF16, NE>(a.q_in, base, x);
   if (!IN_BF16 && !a.rope_fp32) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = bf16_round(x[j]);
+    for (int j = 0; j < NE; ++j) x[j] = bf16_round(x[j]);
   }
 
   if (a.R > 0) {
     const int rs = D - a.R;
-    const int pos = min(token_position(a.cu, a.B, a.T, t), a.max_pos - 1);
+    // a wave's vectors normally belong to one token: then its position is found once,
+    // on the scalar unit
+    const int t0 = __builtin_amdgcn_readfirstlane(t);
+    const int tpos = __all(t == t0) ? token_position(a.cu, a.B, a.T, t0) : token_position(a.cu, a.B, a.T, t);
+    const int pos = min(tpos, a.max_pos - 1);
     const int half = a.R / 2;
     const float* crow = a.cos_t + (long long)pos * half;
     const float* srow = a.sin_t + (long long)pos * half;
     if (a.interleaved) {
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const int e = 8 * g + j;
+      for (int j = 0; j < NE; j += 2) {
+        const int e = e0 + j;
         if (e >= rs) {
           const int col = (e - rs) / 2;
           const float c = crow[col], s = srow[col];
@@ -127,54 +144,66 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
           x[j + 1] = x2 * c + x1 * s;
         }
       }
-    } else if (8 * g >= rs) {
-      // rotate-half: the partner elements are half a rotation away in the same vector;
-      // they are read from memory (the partner lane's cache lines) rather than shuffled
-      const bool first = 8 * g < rs + half;
-      float p[8];
-      load8<IN_BF16>(a.q_in, base + (first ? half : -half), p);
+    } else if (e0 >= rs) {
+      // rotate-half (NE divides rope_dim / 2, so a lane's elements rotate together): the
+      // partner elements, half a rotation away in the same vector, are read from memory
+      // (the partner lane's cache lines) rather than exchanged between lanes
+      const bool first = e0 < rs + half;
+      float p[NE];
+      load_in<IN_BF16, NE>(a.q_in, base + (first ? half : -half), p);
       if (!IN_BF16 && !a.rope_fp32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = bf16_round(p[j]);
+        for (int j = 0; j < NE; ++j) p[j] = bf16_round(p[j]);
       }
-      const int col = 8 * g - rs - (first ? 0 : half);
-      float c[8], sn[8];
-      load8f(crow + col, c);
-      load8f(srow + col, sn);
+      const int col = e0 - rs - (first ? 0 : half);
+      float c[NE], sn[NE];
+      load_f32<NE>(crow + col, c);
+      load_f32<NE>(srow + col, sn);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = first ? (x[j] * c[j] - p[j] * sn[j]) : (x[j] * c[j] + p[j] * sn[j]);
+      for (int j = 0; j < NE; ++j) x[j] = first ? (x[j] * c[j] - p[j] * sn[j]) : (x[j] * c[j] + p[j] * sn[j]);
     }
     if (!a.rope_fp32) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = bf16_round(x[j]);
+      for (int j = 0; j < NE; ++j) x[j] = bf16_round(x[j]);
     }
   }
 
   if (a.q_f32) {
     float4* o = reinterpret_cast<float4*>(a.q_f32 + base);
-    o[0] = make_float4(x[0], x[1], x[2], x[3]);
-    o[1] = make_float4(x[4], x[5], x[6], x[7]);
+#pragma unroll
+    for (int c = 0; c < NE / 4; ++c) o[c] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
   }
 
   if (PREC == kPrecBF16) {
-    uint32_t w[4];
+    uint32_t w[NE / 2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NE / 2; ++j)
       w[j] = (uint32_t)f32_to_bf16_rne(x[2 * j]) | ((uint32_t)f32_to_bf16_rne(x[2 * j + 1]) << 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op) + base) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    float amax = 0.f;
+    uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op) + base);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
-    // per-vector scale: all G lanes of the vector; per-32 scale: the 4 lanes of the block
-    amax = group_amax<(PREC == kPrecFP8) ? G : 4>(amax);
-    const int e = ue8m0_exponent(amax);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.q_op) + base) = e4m3_pack8(x, e);
+    for (int c = 0; c < NE / 8; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+  } else {
+    uint32_t w[NE / 4];
     if (PREC == kPrecFP8) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < NE; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      amax = group_amax<G>(amax);                // the vector's G lanes
+      const int e = ue8m0_exponent(amax);
+      e4m3_pack<NE>(x, e, w);
       if (g == 0) a.q_scale[v] = (uint8_t)(e + 127);
     } else {
-      if ((g & 3) == 0) a.q_scale[v * (D / 32) + g / 4] = (uint8_t)(e + 127);
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < NE; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      amax = group_amax<32 / NE>(amax);          // the lanes of one 32-element block
+      const int e = ue8m0_exponent(amax);
+      e4m3_pack<NE>(x, e, w);
+      if (g % (32 / NE) == 0) a.q_scale[v * (D / 32) + g / (32 / NE)] = (uint8_t)(e + 127);
     }
+    uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.q_op) + base);
+#pragma unroll
+    for (int c = 0; c < NE / 16; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
   }
 }
 
@@ -324,20 +353,26 @@ __device__ __forceinline__ void preprocess_k(const PreArgs& a, int block) {
 }
 
 // One launch: the first blocks preprocess keys (16 tokens each), the rest queries.
-template <int D, bool IN_BF16, int PREC>
+template <int D, bool IN_BF16, int PREC, int NE>
 __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a, int k_blocks) {
   if ((int)blockIdx.x < k_blocks) preprocess_k<D, IN_BF16, PREC>(a, blockIdx.x);
-  else preprocess_q<D, IN_BF16, PREC>(a, blockIdx.x - k_blocks);
+  else preprocess_q<D, IN_BF16, PREC, NE>(a, blockIdx.x - k_blocks);
+}
+
+template <int D, bool IN_BF16, int PREC, int NE>
+hipError_t launch_pre_ne(const PreArgs& a, hipStream_t st) {
+  constexpr int qvpb = 256 / (D / NE);           // query vectors per block
+  const long long q_blocks = (a.q_in && a.T > 0) ? ((long long)a.T * a.H + qvpb - 1) / qvpb : 0;
+  const long long k_blocks = (a.k_in && a.S > 0) ? (a.S + 15) / 16 : 0;
+  if (q_blocks + k_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((preprocess_kernel<D, IN_BF16, PREC, NE>), dim3((unsigned)(q_blocks + k_blocks)), dim3(256), 0,
+                     st, a, (int)k_blocks);
+  return hipGetLastError();
 }
 
 template <int D, bool IN_BF16, int PREC>
 hipError_t launch_pre(const PreArgs& a, hipStream_t st) {
-  const long long q_blocks = (a.q_in && a.T > 0) ? ((long long)a.T * a.H + (256 / (D / 8)) - 1) / (256 / (D / 8)) : 0;
-  const long long k_blocks = (a.k_in && a.S > 0) ? (a.S + 15) / 16 : 0;
-  if (q_blocks + k_blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((preprocess_kernel<D, IN_BF16, PREC>), dim3((unsigned)(q_blocks + k_blocks)), dim3(256), 0, st,
-                     a, (int)k_blocks);
-  return hipGetLastError();
+  return launch_pre_ne<D, IN_BF16, PREC, 16>(a, st);
 }
 
 template <int D, bool IN_BF16>

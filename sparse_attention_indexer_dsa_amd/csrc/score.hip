@@ -300,30 +300,10 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc1[rb][i] = 0.f;
   auto compute = [&](int buf, int c0) {
-    __builtin_amdgcn_sched_barrier(0);
     mma(buf, 0, acc0);
     epilogue(acc1, c0 - 32);
     mma(buf, 1, acc1);
     epilogue(acc0, c0);
-    // Issue order: a wave issues in order and an MFMA occupies the matrix pipe for many
-    // cycles, so each MFMA is followed by a share of the other block's epilogue rather
-    // than the MFMAs of a block being issued back to back.
-    constexpr int NM = 2 * (kFP8 ? KSTEPS : KSTEPS);      // MFMAs per column block
-    constexpr int NR = kFP8 ? 2 * KSTEPS + 1 : KSTEPS;    // LDS reads per column block
-    constexpr int VPM = 72 / NM;                          // epilogue VALU per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
   Stage sa, sb;
   fetch(sa, 0);
