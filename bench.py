@@ -8,11 +8,19 @@ scored and top-k'd per second: pairs = sum over queries of their causal candidat
 or pools for KPool). The default workload is 2 x 4096 tokens, 64 heads, head dim 128,
 key LayerNorm + RoPE (64 dims) in fp32, FP8 E4M3 with per-vector UE8M0 scales, topk 512.
 
-Prints ONE JSON line. Per-kernel times come from HIP events recorded on the stream the
-kernels run on, around each library call, averaged over the timed steps. The roofline
-entry is for the scoring kernel (MFMA-bound): algorithmic flops 2*H*D per pair.
+Prints ONE JSON line. The timed steps replay one step captured as a HIP graph. Per-kernel
+times come from HIP events recorded on the stream the kernels run on, around each library
+call, over the same number of eager steps queued behind a spin kernel, averaged. The
+roofline entry is for the scoring kernel (MFMA-bound): algorithmic flops 2*H*D per pair.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+
+Traffic counters (HBM bytes of the scoring kernel): run the bench twice under
+`rocprofv3 --pmc FETCH_SIZE` and `rocprofv3 --pmc WRITE_SIZE` with `--copy-mb N`, which adds
+one plain device-to-device copy of N MiB after the timed steps as the calibration kernel,
+then `python bench.py --ingest-pmc FETCH_DB WRITE_DB --copy-mb N [--workload W]` scales the
+scoring kernel's counters by the copy kernel's and records them in profiles/traffic.json
+(keyed by workload, tied to the scoring kernel's source hash).
 """
 
 import argparse
@@ -52,7 +60,7 @@ def pair_count(cu, kp):
     return tot
 
 
-def run_gpu(inp, steps, warmup):
+def run_gpu(inp, steps, warmup, copy_mb=0):
     import torch
     import sparse_attention_indexer_dsa_amd as dsa
     import parity
@@ -114,13 +122,39 @@ def run_gpu(inp, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    # One step captured as a HIP graph (the library allocates and synchronises nothing, so a
+    # step captures as is): the timed steps replay it, without host gaps between kernels.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # Per-kernel durations: the same steps run eagerly with HIP events around every library
+    # call on the stream the kernels run on, queued behind a spin kernel so that the stream
+    # never waits for the host between a kernel and its events.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda._sleep(20_000_000)
     for s in range(steps):
         step(events[s])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if copy_mb > 0:     # calibration kernel for the traffic counters (outside the timed steps)
+        n = copy_mb << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     names = ["preprocess", "kpool", "score", "topk"]
     per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])) / 1e3
            for i, n in enumerate(names)}
@@ -187,6 +221,43 @@ def cpu_baseline(inp, budget_s):
             "seconds": round(t_keys + t_rows, 2)}
 
 
+def ingest_pmc(fetch_db, write_db, copy_mb, workload):
+    """Scoring-kernel HBM bytes per launch from two rocprofv3 --pmc databases (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for the copy
+    kernel of copy_mb MiB; recorded in profiles/traffic.json for the workload."""
+    import sqlite3
+    import gen
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
+        out = {}
+        for name, cname, val in rows:
+            if cname == counter:
+                out.setdefault(name, []).append(float(val))
+        return out
+
+    res = {}
+    for db, counter in ((fetch_db, "FETCH_SIZE"), (write_db, "WRITE_SIZE")):
+        k = per_kernel(db, counter)
+        score = [v for n, vs in k.items() if "score_kernel" in n for v in vs]
+        copy = [v for n, vs in k.items() if "copybuffer" in n.lower() for v in vs]
+        if not score or not copy:
+            raise SystemExit(f"{db}: no {counter} records for the scoring or the copy kernel")
+        copy_kib = max(copy)                       # the calibration copy is the largest copy
+        factor = copy_mb * 1024.0 / copy_kib
+        res[counter] = {"kib_per_launch": float(np.mean(score)), "copy_kib": copy_kib, "factor": factor,
+                        "bytes_per_launch": float(np.mean(score)) * 1024.0 * factor}
+    name = gen.WORKLOADS[workload]["name"]
+    rec = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    rec[name] = {"bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"],
+                 "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"], "copy_mb": copy_mb,
+                 "source_hash": kernel_source_hash()}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print(json.dumps({name: rec[name]}, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,7 +266,15 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0, help="calibration copy of this many MiB after timing")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="record scoring-kernel traffic from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        if args.copy_mb <= 0:
+            raise SystemExit("--ingest-pmc needs the --copy-mb size of the calibration copy")
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.copy_mb, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the hot path runs on a "
               "single MI355X; sharding across GPUs is a design note, not a measured path)", file=sys.stderr)
@@ -206,7 +285,7 @@ def main():
     kp = inp["kpool"]
     pairs = pair_count(inp["cu_seqlens"], kp)
     print(f"[bench] workload {args.workload}: {inp['name']} T={T} pairs={pairs}", file=sys.stderr, flush=True)
-    elapsed, per = run_gpu(inp, args.steps, args.warmup)
+    elapsed, per = run_gpu(inp, args.steps, args.warmup, args.copy_mb)
     alg = algorithmic(inp, pairs)
     prec = inp["precision"]
     kernels = {}
