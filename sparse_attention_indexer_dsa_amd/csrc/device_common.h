@@ -60,6 +60,20 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
+// ---------------------------------------------------------------- buffers
+
+constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: raw 32-bit data format
+
+// Buffer descriptor over `bytes` bytes at `base` (both wave-uniform; read from lane 0 so the
+// descriptor lives in scalar registers). Loads past `bytes` return zeros, stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t plo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t phi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)phi << 32) | plo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
 // ---------------------------------------------------------------- documents
 
 // Document of token t: the b in [0, B) with cu[b] <= t < cu[b+1] (last such b for empty

@@ -36,7 +36,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kNK = 64;          // keys per LDS tile
 constexpr int kThreads = 256;
-constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: raw 32-bit data format
 
 struct ScoreArgs {
   const void* q_op; const uint8_t* q_scale;
@@ -48,16 +47,6 @@ struct ScoreArgs {
   float* scores; int stride; int max_cand;
   int ntiles;                    // query tiles per document (ceil(max_seqlen / tokens per workgroup))
 };
-
-// Buffer descriptor over `bytes` bytes at `base` (both wave-uniform; read from lane 0 so the
-// descriptor lives in scalar registers). Loads past `bytes` return zeros, stores are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t plo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t phi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  void* q = reinterpret_cast<void*>(((uint64_t)phi << 32) | plo);
-  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
-}
 
 __device__ __forceinline__ float relu(float x) {
   // max(x, 0) on the bit pattern: negative values (sign bit set, -0 included) become +0;

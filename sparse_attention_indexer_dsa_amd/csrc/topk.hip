@@ -1,17 +1,18 @@
 // Per-row top-k selection over the score workspace, with KPool expansion (gfx950).
 //
-// One workgroup per query row. Each thread holds a contiguous chunk of the row's
-// candidates as order-preserving uint32 keys in registers. A three-pass radix select
-// (11 + 11 + 10 bits; LDS histograms with integer atomics, bin search by wave scans) finds
-// the topk-th largest key; every candidate above it is taken and, among candidates equal
-// to it, the lowest indices (deterministic tie breaking, Megatron-LM PR 5992, "Key
-// changes"). Positions in the selection buffer come from block prefix sums, so the
-// kernel uses no floating-point atomics and its result does not depend on scheduling.
-// The selection is sorted by (score descending, index ascending) with a bitonic network
-// whose stages inside a 64- or 256-element segment run in registers (lane shuffles and
-// in-lane exchanges) and only the wider stages go through LDS. Outputs are padded with
-// -1 / -inf. For KPool (PR 7522, "Changes") selected pools are expanded to their tokens
-// and the query's incomplete causal pool is appended when requested.
+// One workgroup per query row. Each thread holds 4-candidate chunks of the row, interleaved
+// across the workgroup, as order-preserving uint32 keys in registers; chunk groups past the
+// row's last candidate are skipped by every pass. The topk-th largest key comes from a
+// 2048-bin histogram linear in the score (LDS integer atomics; the threshold bin's few keys
+// are then ranked exactly), or for clustered rows from an 11 + 11 + 10-bit radix select.
+// Every candidate above it is taken and, among candidates equal to it, the lowest indices
+// (deterministic tie breaking, Megatron-LM PR 5992, "Key changes"). Slots in the selection
+// buffer come from block prefix sums, so the kernel uses no floating-point atomics and its
+// result does not depend on scheduling. The selection is ordered by (score descending,
+// index ascending): buckets linear in the score, a prefix sum, a scatter and an exact rank
+// inside each bucket, or a bitonic network when a bucket is heavy (ties). Outputs are
+// padded with -1 / -inf. For KPool (PR 7522, "Changes") selected pools are expanded to their
+// tokens and the query's incomplete causal pool is appended when requested.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -273,23 +274,6 @@ __device__ __forceinline__ RowInfo row_info(const TopkArgs& a, int t) {
   return r;
 }
 
-// Scores of this thread's chunk [tid*EPT, tid*EPT + EPT) of row r (NaN marks "no candidate").
-template <int EPT>
-__device__ __forceinline__ void load_row(const TopkArgs& a, const RowInfo& r, float (&x)[EPT]) {
-  const float* row = a.scores + (long long)r.t * a.stride;
-  const int i0 = threadIdx.x * EPT;
-  if (EPT % 4 == 0 && i0 + EPT <= r.cand) {
-#pragma unroll
-    for (int e = 0; e < EPT; e += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i0 + e);
-      x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) x[e] = (i0 + e < r.cand) ? row[i0 + e] : __builtin_nanf("");
-  }
-}
-
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -301,26 +285,46 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   int* misc = wsum + 32;                                                     // [8]
 
   const int tid = threadIdx.x;
-  const int i0 = tid * EPT;
   const int topk = a.topk;
   const int kp = a.kpool;
   const int t = blockIdx.x;
   const RowInfo cur = row_info(a, t);
   const int cand = cur.cand, nsel = cur.nsel;
 
-  uint32_t key[EPT];                       // order-preserving keys (0: no candidate)
+  // ---- the row's scores as order-preserving keys (0: no candidate). Thread tid holds the
+  //      4-candidate chunks c = e*NT + tid (candidates 4c .. 4c+3), so one load instruction
+  //      covers 16*NT consecutive bytes, and a chunk group e lies entirely past the row once
+  //      4*e*NT >= cand: such groups are skipped by every per-candidate pass (uniform branch).
+  static_assert(EPT % 4 == 0, "candidates are held in chunks of 4");
+  constexpr int NCH = EPT / 4;
+  auto live = [&](int e) { return 4 * e * NT < cand; };
+  auto idx = [&](int e, int j) { return 4 * (e * NT + tid) + j; };
+  uint32_t key[EPT];
   {
-    float raw[EPT];
-    load_row<EPT>(a, cur, raw);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.scores + (long long)t * a.stride, cand * 4);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) key[e] = (i0 + e < cand) ? score_key(raw[e]) : 0u;
+    for (int e = 0; e < NCH; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * e + j] = 0u;
+      if (live(e)) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rr, (e * NT + tid) * 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) key[4 * e + j] = idx(e, j) < cand ? score_key(u2f(v[j])) : 0u;
+      }
+    }
   }
 
   // ---- key range of the row's candidates (max and min in one reduction)
   uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    if (key[e] != 0u) { kmax = key[e] > kmax ? key[e] : kmax; kmin = key[e] < kmin ? key[e] : kmin; }
+  for (int e = 0; e < NCH; ++e) {
+    if (live(e)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k = key[4 * e + j];
+        if (k != 0u) { kmax = k > kmax ? k : kmax; kmin = k < kmin ? k : kmin; }
+      }
+    }
   }
   block_minmax<NT>(kmin, kmax, wsum);
 
@@ -343,8 +347,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       if (tid == 0) misc[5] = 0;
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if (bin[e] >= 0) atomicAdd(&hist[bin[e]], 1u);
+      for (int e = 0; e < NCH; ++e)
+        if (live(e)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (bin[4 * e + j] >= 0) atomicAdd(&hist[bin[4 * e + j]], 1u);
+        }
       __syncthreads();
       find_rank_bin<NT, 2048>(hist, krem, wsum, misc);
       const int d1 = misc[0];
@@ -354,8 +362,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         // the threshold bin's candidates to a list (order irrelevant), then one wave finds
         // the krem1-th largest among them by counting over lane values
 #pragma unroll
-        for (int e = 0; e < EPT; ++e)
-          if (bin[e] == d1) aux[atomicAdd(&misc[5], 1)] = key[e];
+        for (int e = 0; e < NCH; ++e)
+          if (live(e)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (bin[4 * e + j] == d1) aux[atomicAdd(&misc[5], 1)] = key[4 * e + j];
+          }
         __syncthreads();
         if (tid < 64) {
           const uint32_t k = tid < c1 ? aux[tid] : 0u;
@@ -390,10 +402,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         for (int i = tid; i < 2048; i += NT) hist[i] = 0;
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          const uint32_t k = key[e];
-          if (k != 0u && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
-        }
+        for (int e = 0; e < NCH; ++e)
+          if (live(e)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t k = key[4 * e + j];
+              if (k != 0u && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+            }
+          }
         __syncthreads();
         find_rank_bin<NT, 2048>(hist, krem, wsum, misc);
         krem -= misc[1];
@@ -406,28 +422,83 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     krem = cand;   // every candidate is taken
   }
 
-  // ---- compaction in index order: keys above thr, then the first krem keys equal to thr.
-  //      Positions come from one block prefix sum of (above << 16 | equal) counts.
-  int packed = 0;
+  // ---- compaction into selB[0, nsel): keys above thr (in any order: the ordering pass
+  //      sorts them), then the krem lowest-index keys equal to thr. One block prefix sum of
+  //      (above << 16 | equal) counts gives every thread its slots; only when fewer equal
+  //      keys are taken than exist is their index order needed, from a second prefix sum
+  //      with one count field per chunk group (index order is group-major).
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) packed += key[e] > thr ? (1 << 16) : ((key[e] == thr && key[e] != 0u) ? 1 : 0);
-  int tot;
-  const int before = block_exclusive_sum<NT>(packed, wsum, tot);
-  {
-    const int ngt = tot >> 16;
-    int pos_gt = before >> 16;
-    int rank_eq = before & 0xFFFF;
+  for (int e = 0; e < NCH; ++e)
+    if (live(e)) {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t k = key[e];
-      const u64 v = ((u64)(~k) << 32) | (uint32_t)(i0 + e);
-      if (k > thr) {
-        selB[pos_gt++] = v;
-      } else if (k == thr && k != 0u) {
-        if (rank_eq < krem) selB[ngt + rank_eq] = v;
-        ++rank_eq;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k = key[4 * e + j];
+        n_gt += k > thr;
+        n_eq += k == thr && k != 0u;
       }
     }
+  int tot;
+  const int before = block_exclusive_sum<NT>((n_gt << 16) | n_eq, wsum, tot);
+  const int ngt = tot >> 16, neq = tot & 0xFFFF;
+  int pos_gt = before >> 16;
+  if (neq <= krem) {
+    int pos_eq = ngt + (before & 0xFFFF);
+#pragma unroll
+    for (int e = 0; e < NCH; ++e)
+      if (live(e)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t k = key[4 * e + j];
+          const u64 v = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+          if (k > thr) selB[pos_gt++] = v;
+          else if (k == thr && k != 0u) selB[pos_eq++] = v;
+        }
+      }
+  } else {
+    // group e's equal keys come after all equal keys of groups < e; inside group e, thread
+    // order then position in the chunk. Fields of 16 bits, two groups per prefix sum.
+    int eq_before_group = 0;
+#pragma unroll
+    for (int e2 = 0; e2 < NCH; e2 += 2) {
+      int c0 = 0, c1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k0 = key[4 * e2 + j];
+        c0 += k0 == thr && k0 != 0u;
+        if (e2 + 1 < NCH) {
+          const uint32_t k1 = key[4 * (e2 + 1) + j];
+          c1 += k1 == thr && k1 != 0u;
+        }
+      }
+      int gtot;
+      const int gb = block_exclusive_sum<NT>((c1 << 16) | c0, wsum, gtot);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = e2 + h;
+        if (e < NCH) {
+          int rank = eq_before_group + ((h ? gb >> 16 : gb & 0xFFFF));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t k = key[4 * e + j];
+            if (k == thr && k != 0u) {
+              if (rank < krem) selB[ngt + rank] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+              ++rank;
+            }
+          }
+          eq_before_group += h ? gtot >> 16 : gtot & 0xFFFF;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NCH; ++e)
+      if (live(e)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t k = key[4 * e + j];
+          if (k > thr) selB[pos_gt++] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+        }
+      }
   }
 
   // ---- ordering of selB[0, nsel): bucket b = floor((vmax - score) * scale) over
@@ -592,9 +663,7 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
   a.out_pool_indices = p.out_pool_indices;
   const int mc = p.max_cand;
   const size_t lds = topk_lds_bytes(p.max_cand, p.topk);
-  if (mc <= 256) return launch_cfg<256, 1>(a, lds, st);
-  if (mc <= 512) return launch_cfg<256, 2>(a, lds, st);
-  if (mc <= 1024) return launch_cfg<256, 4>(a, lds, st);
+  if (mc <= 1024) return launch_cfg<256, 4>(a, lds, st);   // chunks of 4: at least 4 per thread
   if (mc <= 2048) return launch_cfg<256, 8>(a, lds, st);
   if (mc <= 4096) return launch_cfg<256, 16>(a, lds, st);
   if (mc <= 8192) return launch_cfg<512, 16>(a, lds, st);
