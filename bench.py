@@ -60,7 +60,7 @@ def pair_count(cu, kp):
     return tot
 
 
-def run_gpu(inp, steps, warmup, copy_mb=0):
+def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False):
     import torch
     import sparse_attention_indexer_dsa_amd as dsa
     import parity
@@ -74,13 +74,16 @@ def run_gpu(inp, steps, warmup, copy_mb=0):
     nsb = {"bf16": 0, "fp8": 1, "mxfp8": D // 32}[prec]
     odt = torch.bfloat16 if prec == "bf16" else torch.uint8
     ops = {}
-    if inp["preprocess"]:
+    fused = inp["preprocess"] and kp == 1 and fuse
+    if inp["preprocess"] and not fused:
         ops["q_op"] = torch.empty((T, H, D), dtype=odt, device=dev)
+    if inp["preprocess"]:
         ops["k_op"] = torch.empty((T, D), dtype=odt, device=dev)
         if prec != "bf16":
-            ops["q_scale"] = torch.empty((T, H) if prec == "fp8" else (T, H, nsb), dtype=torch.uint8, device=dev)
+            if not fused:
+                ops["q_scale"] = torch.empty((T, H) if prec == "fp8" else (T, H, nsb), dtype=torch.uint8, device=dev)
             ops["k_scale"] = torch.empty((T,) if prec == "fp8" else (T, nsb), dtype=torch.uint8, device=dev)
-        q_op, k_src = ops["q_op"], ops["k_op"]
+        q_op, k_src = ops.get("q_op"), ops["k_op"]
     else:
         q_op, k_src = d["q"], d["k"]
     pool = {}
@@ -100,7 +103,9 @@ def run_gpu(inp, steps, warmup, copy_mb=0):
         if ev is not None:
             ev[i].record(); i += 1
         if inp["preprocess"]:
-            dsa.preprocess(d["q"], d["k"], d["cu"], ln_gamma=d.get("gamma") if inp["layernorm"] else None,
+            # fused: only the keys here; the scoring kernel preprocesses the queries itself
+            dsa.preprocess(None if fused else d["q"], d["k"], d["cu"],
+                           ln_gamma=d.get("gamma") if inp["layernorm"] else None,
                            ln_beta=d.get("beta") if inp["layernorm"] else None, ln_eps=1e-6,
                            rope_cos=d.get("cos"), rope_sin=d.get("sin"), rope_dim=inp["rope_dim"],
                            rope_fp32=inp["rope_fp32"], precision=prec, out=ops)
@@ -110,8 +115,13 @@ def run_gpu(inp, steps, warmup, copy_mb=0):
             dsa.kpool(k_src, d["cu"], d["gate"], d["bias"], kp, precision=prec, out=pool)
         if ev is not None:
             ev[i].record(); i += 1
-        dsa.score(q_op, k_op, d["w"], d["cu"], max_seqlen, ws, q_scale=ops.get("q_scale"), k_scale=k_scale,
-                  precision=prec, kpool=kp, cu_pools=pool.get("cu_pools"))
+        if fused:
+            dsa.score_fused(d["q"], k_op, d["w"], d["cu"], max_seqlen, ws, k_scale=k_scale, rope_cos=d.get("cos"),
+                            rope_sin=d.get("sin"), rope_dim=inp["rope_dim"], rope_fp32=inp["rope_fp32"],
+                            precision=prec)
+        else:
+            dsa.score(q_op, k_op, d["w"], d["cu"], max_seqlen, ws, q_scale=ops.get("q_scale"), k_scale=k_scale,
+                      precision=prec, kpool=kp, cu_pools=pool.get("cu_pools"))
         if ev is not None:
             ev[i].record(); i += 1
         dsa.topk(ws, T, d["cu"], max_seqlen, topk, kpool=kp, cu_pools=pool.get("cu_pools"), kpool_tail=True,
@@ -158,24 +168,28 @@ def run_gpu(inp, steps, warmup, copy_mb=0):
     names = ["preprocess", "kpool", "score", "topk"]
     per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])) / 1e3
            for i, n in enumerate(names)}
-    return (t1 - t0), per
+    return (t1 - t0), per, fused
 
 
-def algorithmic(inp, pairs):
-    """Algorithmic flops/bytes per launch of each kernel (measurement)."""
+def algorithmic(inp, pairs, fused):
+    """Algorithmic flops/bytes per launch of each kernel. Fused: the preprocessing kernel
+    handles the keys only and the scoring kernel reads the raw (bf16) queries."""
     T, H, D = inp["q"].shape
     prec, kp, topk = inp["precision"], inp["kpool"], inp["topk"]
     esz = 2 if prec == "bf16" else 1
     nsb = {"bf16": 0, "fp8": 1, "mxfp8": D // 32}[prec]
     out = {"score_flops": 2.0 * H * D * pairs}
     if inp["preprocess"]:
-        out["preprocess_bytes"] = float(T * H * D * 2 + T * H * D * esz + T * H * nsb + T * D * 2 + T * D * esz + T * nsb)
+        out["preprocess_bytes"] = float(T * D * 2 + T * D * esz + T * nsb)
+        if not fused:
+            out["preprocess_bytes"] += float(T * H * D * 2 + T * H * D * esz + T * H * nsb)
     if kp > 1:
         P = T // kp
         out["kpool_bytes"] = float(T * D * 2 + T * 2 + P * D * esz)
     width = topk if kp == 1 else topk * kp + kp - 1
     out["topk_bytes"] = float(pairs * 4 + T * topk * 4 + T * width * 4 + T * 4 + (T * topk * 4 if kp > 1 else 0))
-    out["score_bytes"] = float(T * H * D * esz + T * H * 4 + (T // kp) * D * esz + pairs * 4)
+    q_bytes = T * H * D * 2 if fused else T * H * D * esz + T * H * nsb
+    out["score_bytes"] = float(q_bytes + T * H * 4 + (T // kp) * D * esz + pairs * 4)
     return out
 
 
@@ -267,6 +281,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0, help="calibration copy of this many MiB after timing")
+    ap.add_argument("--fuse", action="store_true",
+                    help="preprocess the queries inside the scoring kernel (dsa_index_score_fused) instead of in "
+                         "the preprocessing kernel")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="record scoring-kernel traffic from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
@@ -285,8 +302,8 @@ def main():
     kp = inp["kpool"]
     pairs = pair_count(inp["cu_seqlens"], kp)
     print(f"[bench] workload {args.workload}: {inp['name']} T={T} pairs={pairs}", file=sys.stderr, flush=True)
-    elapsed, per = run_gpu(inp, args.steps, args.warmup, args.copy_mb)
-    alg = algorithmic(inp, pairs)
+    elapsed, per, fused = run_gpu(inp, args.steps, args.warmup, args.copy_mb, args.fuse)
+    alg = algorithmic(inp, pairs, fused)
     prec = inp["precision"]
     kernels = {}
     for n in ("preprocess", "kpool", "score", "topk"):
@@ -322,7 +339,9 @@ def main():
         "data": "synthetic (seeded numpy draws with the workload's shapes and distributions)",
         "config": {"workload": inp["name"], "T": T, "H": H, "D": D, "docs": inp["docs"] if len(inp["docs"]) <= 16
                    else f"{len(inp['docs'])} docs", "topk": inp["topk"], "kpool": kp, "precision": prec,
-                   "preprocess": bool(inp["preprocess"]), "pairs_per_step": pairs, "parallelism": "single GPU"},
+                   "preprocess": bool(inp["preprocess"]), "query_preprocessing": "in the scoring kernel" if fused
+                   else ("own kernel" if inp["preprocess"] else "none"), "pairs_per_step": pairs,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "score", "achieved": round(achieved, 2),
                      "peak": PEAK_FLOPS[prec] / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved * 1e12 / PEAK_FLOPS[prec], 4), "traffic": traffic},

@@ -234,6 +234,70 @@ dsa_status_t dsa_index_topk(
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* dsa_last_error(void);
 
+/*
+ * dsa_index_score_fused - dsa_index_score with the query preprocessing fused into the
+ * scoring kernel: it takes the raw queries q_in [T,H,D] (bf16 or fp32, in_dtype, 16-byte
+ * aligned) and the RoPE arguments of dsa_index_preprocess instead of q_op / q_scale, and
+ * builds each query's operands (RoPE, carrier rounding, quantisation) in registers, byte-
+ * identical to those dsa_index_preprocess writes. The keys (k_op, k_scale) come
+ * preprocessed as for dsa_index_score (kpool 1). Writes the same workspace rows as
+ * dsa_index_score. q_op_out / q_scale_out: optional copies of the query operands built
+ * (as for dsa_index_forward; NULL: not written). Errors as for dsa_index_score, plus the
+ * RoPE restriction of dsa_index_forward.
+ */
+dsa_status_t dsa_index_score_fused(
+    const void* q_in, dsa_dtype_t in_dtype,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    const float* rope_cos, const float* rope_sin,
+    int32_t rope_dim, int32_t rope_max_pos, int32_t rope_interleaved, int32_t rope_fp32,
+    float sm_scale, dsa_precision_t precision,
+    void* q_op_out, uint8_t* q_scale_out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_index_forward - the whole indexer hot path in one call, for kpool == 1: the keys are
+ * preprocessed (LayerNorm, RoPE, quantisation, as dsa_index_preprocess) into the workspace,
+ * the scoring kernel preprocesses each query vector itself (RoPE, quantisation) straight
+ * into its MFMA operands, so quantised queries never go through memory, and the top-k
+ * follows (the steps the pages describe for the indexer forward: preprocessing, scoring,
+ * top-k; Megatron-LM PR 8403 "What does this PR do?", PR 5992 "Key changes"). Results are
+ * those of dsa_index_preprocess + dsa_index_score_topk with the same arguments (operands
+ * byte-identical, hence identical scores and selections).
+ *
+ *   q_in [T,H,D], k_in [T,D]  bf16 or fp32 (in_dtype), 16-byte aligned; queries and keys
+ *             share cu_seqlens (S = T).
+ *   w, cu_seqlens, num_seqs, max_seqlen, topk, sm_scale, precision: as for
+ *             dsa_index_score_topk; ln_*, rope_*: as for dsa_index_preprocess.
+ *   out_indices [T,topk], out_scores [T,topk], out_lengths [T]: as for dsa_index_score_topk.
+ *   q_op_out, q_scale_out: optional (NULL: not written). When given, the quantised query
+ *             operands the scoring kernel built ([T,H,D] bf16 or E4M3 bytes, 16-byte
+ *             aligned; scales [T,H] or [T,H,D/32]) for rows of tokens at positions
+ *             < max_seqlen; other rows are not written.
+ *   workspace  >= dsa_index_forward_workspace_size(T, D, max_seqlen, precision) bytes,
+ *             256-byte aligned (score rows, then quantised keys and scales).
+ * Errors as for dsa_index_score_topk; DSA_ERR_UNSUPPORTED also for rotate-half RoPE with
+ * an fp8 precision when rope_dim % 64 != 0 (the two halves of a rotated pair then sit in
+ * different lanes of the MFMA operand layout; the two-call path supports it).
+ */
+size_t dsa_index_forward_workspace_size(int32_t T, int32_t D, int32_t max_seqlen,
+                                        dsa_precision_t precision);
+
+dsa_status_t dsa_index_forward(
+    const void* q_in, const void* k_in, dsa_dtype_t in_dtype,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    const float* ln_gamma, const float* ln_beta, float ln_eps,
+    const float* rope_cos, const float* rope_sin,
+    int32_t rope_dim, int32_t rope_max_pos, int32_t rope_interleaved, int32_t rope_fp32,
+    int32_t topk, float sm_scale, dsa_precision_t precision,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths,
+    void* q_op_out, uint8_t* q_scale_out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

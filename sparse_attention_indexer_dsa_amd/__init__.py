@@ -25,8 +25,8 @@ import os
 
 import torch
 
-__all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "topk", "library_path", "load",
-           "PRECISIONS", "DsaError"]
+__all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "score_fused", "topk", "forward",
+           "forward_workspace_size", "library_path", "load", "PRECISIONS", "DsaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libdsa_index.so"
@@ -70,6 +70,14 @@ def load():
                                     f32, i32, vp, sz, vp]
     lib.dsa_index_topk.restype = i32
     lib.dsa_index_topk.argtypes = [vp, sz, i32, vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.dsa_index_forward_workspace_size.restype = sz
+    lib.dsa_index_forward_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dsa_index_forward.restype = i32
+    lib.dsa_index_forward.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, i32, i32, vp, vp, f32, vp, vp,
+                                      i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_index_score_fused.restype = i32
+    lib.dsa_index_score_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32,
+                                          i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_last_error.argtypes = []
     _lib = lib
@@ -248,6 +256,82 @@ def score_topk(q_op, k_op, w, cu_seqlens, max_seqlen, topk, *, q_scale=None, k_s
         _ptr(out.get("pool_indices")), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(dev))
     _check(st, "dsa_index_score_topk")
+    return out
+
+
+def score_fused(q, k_op, w, cu_seqlens, max_seqlen, workspace, *, k_scale=None, rope_cos=None, rope_sin=None,
+                rope_dim=0, rope_interleaved=False, rope_fp32=False, precision="bf16", sm_scale=1.0,
+                out_operands=None):
+    """Scores into ``workspace`` from raw queries q [T,H,D] (the query preprocessing runs inside
+    the scoring kernel) and preprocessed keys. ``out_operands`` may hold 'q_op' / 'q_scale'
+    tensors to receive the query operands the kernel built."""
+    lib = load()
+    prec = _prec(precision)
+    T, H, D = q.shape
+    S = k_op.shape[0]
+    if q.dtype not in _DTYPES or w.dtype not in _DTYPES:
+        raise ValueError("q and w must be bf16 or fp32")
+    for name, t in (("q", q), ("k_op", k_op), ("w", w), ("k_scale", k_scale)):
+        _need(t, name)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,))
+    ops = out_operands or {}
+    max_pos = rope_cos.shape[0] if (rope_cos is not None and rope_dim) else 0
+    st = lib.dsa_index_score_fused(
+        _ptr(q), _DTYPES[q.dtype], _ptr(k_op), _ptr(k_scale), _ptr(w), _DTYPES[w.dtype], T, S, H, D,
+        _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), _ptr(rope_cos), _ptr(rope_sin), int(rope_dim),
+        int(max_pos), int(bool(rope_interleaved)), int(bool(rope_fp32)), float(sm_scale), prec,
+        _ptr(ops.get("q_op")), _ptr(ops.get("q_scale")), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, "dsa_index_score_fused")
+    return workspace
+
+
+def forward_workspace_size(T, D, max_seqlen, precision="bf16"):
+    """Bytes of workspace `forward` needs."""
+    return int(load().dsa_index_forward_workspace_size(int(T), int(D), int(max_seqlen), _prec(precision)))
+
+
+def forward(q, k, w, cu_seqlens, max_seqlen, topk, *, ln_gamma=None, ln_beta=None, ln_eps=1e-6,
+            rope_cos=None, rope_sin=None, rope_dim=0, rope_interleaved=False, rope_fp32=False,
+            precision="bf16", sm_scale=1.0, return_operands=False, workspace=None, out=None):
+    """The whole hot path in one call (kpool 1): key preprocessing, scoring with the query
+    preprocessing done inside the scoring kernel, top-k.
+
+    Returns a dict with 'indices' [T,topk], 'scores' [T,topk], 'lengths' [T] and, with
+    ``return_operands``, the query operands the scoring kernel built ('q_op', 'q_scale').
+    """
+    lib = load()
+    prec = _prec(precision)
+    T, H, D = q.shape
+    dev = q.device
+    if q.dtype not in _DTYPES or k.dtype != q.dtype:
+        raise ValueError(f"q and k must both be bf16 or both fp32, got {q.dtype} and {k.dtype}")
+    if w.dtype not in _DTYPES:
+        raise ValueError(f"w must be bf16 or fp32, got {w.dtype}")
+    for name, t in (("q", q), ("k", k), ("w", w)):
+        _need(t, name)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,))
+    for name, t in (("ln_gamma", ln_gamma), ("ln_beta", ln_beta), ("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        _need(t, name, (torch.float32,))
+    out = _alloc_outputs(out, T, topk, 1, dev)
+    if return_operands:
+        out.setdefault("q_op", torch.empty((T, H, D), dtype=_op_dtype(prec), device=dev))
+        if prec != 0:
+            out.setdefault("q_scale", torch.empty((T, H) if prec == 1 else (T, H, D // 32), dtype=torch.uint8,
+                                                  device=dev))
+    need = forward_workspace_size(T, D, max_seqlen, precision)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    max_pos = rope_cos.shape[0] if (rope_cos is not None and rope_dim) else 0
+    st = lib.dsa_index_forward(
+        _ptr(q), _ptr(k), _DTYPES[q.dtype], _ptr(w), _DTYPES[w.dtype], T, H, D, _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, int(max_seqlen), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps), _ptr(rope_cos),
+        _ptr(rope_sin), int(rope_dim), int(max_pos), int(bool(rope_interleaved)), int(bool(rope_fp32)), int(topk),
+        float(sm_scale), prec, _ptr(out["indices"]), _ptr(out["scores"]), _ptr(out["lengths"]),
+        _ptr(out.get("q_op")), _ptr(out.get("q_scale")), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "dsa_index_forward")
+    out["workspace"] = workspace
     return out
 
 

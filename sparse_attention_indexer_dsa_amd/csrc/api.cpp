@@ -319,4 +319,144 @@ dsa_status_t dsa_index_score_topk(
   return DSA_OK;
 }
 
+namespace {
+
+dsa_status_t check_fused_rope(int precision, int D, const float* rope_cos, const float* rope_sin, int rope_dim,
+                              int rope_max_pos, int rope_interleaved) {
+  if (rope_dim < 0 || rope_dim > D || (rope_dim % 2) != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "rope_dim=%d must be even and within [0, D=%d]", rope_dim, D);
+  if (rope_dim > 0 && !rope_interleaved && rope_dim % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "rotate-half RoPE needs rope_dim %% 32 == 0 (got %d)", rope_dim);
+  if (!dsa::score_can_fuse_rope(precision, rope_dim, rope_interleaved ? 1 : 0))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "rotate-half RoPE over %d dims with an fp8 precision needs rope_dim %% 64 == 0 here; use "
+                "dsa_index_preprocess + dsa_index_score_topk", rope_dim);
+  if (rope_dim > 0 && (!rope_cos || !rope_sin || rope_max_pos < 1))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "rope tables and rope_max_pos >= 1 required when rope_dim > 0");
+  if (rope_dim > 0 && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "rope tables must be 16-byte aligned");
+  return DSA_OK;
+}
+
+void set_fused_q(dsa::ScoreTopkLaunch& p, const void* q_in, dsa_dtype_t in_dtype, const float* rope_cos,
+                 const float* rope_sin, int rope_dim, int rope_max_pos, int rope_interleaved, int rope_fp32,
+                 void* q_op_out, uint8_t* q_scale_out) {
+  p.q_in = q_in; p.in_bf16 = in_dtype == DSA_DTYPE_BF16;
+  p.cos_t = rope_cos; p.sin_t = rope_sin;
+  p.rope_dim = rope_dim; p.max_pos = rope_max_pos; p.interleaved = rope_interleaved ? 1 : 0;
+  p.rope_fp32 = rope_fp32 ? 1 : 0;
+  p.q_op_out = q_op_out; p.q_scale_out = q_scale_out;
+}
+
+}  // namespace
+
+dsa_status_t dsa_index_score_fused(
+    const void* q_in, dsa_dtype_t in_dtype,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    const float* rope_cos, const float* rope_sin,
+    int32_t rope_dim, int32_t rope_max_pos, int32_t rope_interleaved, int32_t rope_fp32,
+    float sm_scale, dsa_precision_t precision,
+    void* q_op_out, uint8_t* q_scale_out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_precision((int)precision)) != DSA_OK) return st;
+  if (in_dtype != DSA_DTYPE_BF16 && in_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "in_dtype %d must be bf16 (0) or fp32 (1)", (int)in_dtype);
+  // the operand checks of dsa_index_score, with q_in standing for the (absent) q operands
+  if ((st = check_score_args(q_in, static_cast<const uint8_t*>(q_in), k_op, k_scale, w, w_dtype, T, S, H, D,
+                             (int)precision, workspace)) != DSA_OK)
+    return st;
+  if ((st = check_fused_rope((int)precision, D, rope_cos, rope_sin, rope_dim, rope_max_pos, rope_interleaved)) != DSA_OK)
+    return st;
+  if ((st = check_geometry(T, cu_seqlens, num_seqs, max_seqlen, 1, nullptr, 1, false)) != DSA_OK) return st;
+  if (T == 0) return DSA_OK;
+  if (q_op_out && !aligned(q_op_out, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "q_op_out must be 16-byte aligned");
+  const size_t need = dsa_index_workspace_size(T, H, D, num_seqs, max_seqlen, 1, 1, precision);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  dsa::ScoreTopkLaunch p = make_launch(nullptr, nullptr, k_op, k_scale, w, w_dtype, T, S, H, D, cu_seqlens,
+                                       num_seqs, max_seqlen, 1, nullptr, 0, 1, sm_scale, (int)precision, nullptr,
+                                       nullptr, nullptr, nullptr, workspace);
+  set_fused_q(p, q_in, in_dtype, rope_cos, rope_sin, rope_dim, rope_max_pos, rope_interleaved, rope_fp32,
+              q_op_out, q_scale_out);
+  hipError_t e = dsa::launch_score(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score_fused");
+  return DSA_OK;
+}
+
+size_t dsa_index_forward_workspace_size(int32_t T, int32_t D, int32_t max_seqlen, dsa_precision_t precision) {
+  if (T < 0 || max_seqlen < 0 || (D != 64 && D != 128)) return 0;
+  const size_t es = precision == DSA_PREC_BF16 ? 2 : 1;
+  const size_t nsb = precision == DSA_PREC_BF16 ? 0 : (precision == DSA_PREC_FP8 ? 1 : (size_t)D / 32);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t scores = (size_t)T * (size_t)row_stride(max_seqlen) * sizeof(float);
+  return up(scores) + up((size_t)T * D * es) + up((size_t)T * nsb) + 256;
+}
+
+dsa_status_t dsa_index_forward(
+    const void* q_in, const void* k_in, dsa_dtype_t in_dtype,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    const float* ln_gamma, const float* ln_beta, float ln_eps,
+    const float* rope_cos, const float* rope_sin,
+    int32_t rope_dim, int32_t rope_max_pos, int32_t rope_interleaved, int32_t rope_fp32,
+    int32_t topk, float sm_scale, dsa_precision_t precision,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths,
+    void* q_op_out, uint8_t* q_scale_out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_precision((int)precision)) != DSA_OK) return st;
+  if (in_dtype != DSA_DTYPE_BF16 && in_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "in_dtype %d must be bf16 (0) or fp32 (1)", (int)in_dtype);
+  if (w_dtype != DSA_DTYPE_BF16 && w_dtype != DSA_DTYPE_FP32)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "w_dtype %d must be bf16 (0) or fp32 (1)", (int)w_dtype);
+  if ((st = check_hd(H, D, true)) != DSA_OK) return st;
+  if ((st = check_fused_rope((int)precision, D, rope_cos, rope_sin, rope_dim, rope_max_pos, rope_interleaved)) != DSA_OK)
+    return st;
+  if ((st = check_geometry(T, cu_seqlens, num_seqs, max_seqlen, 1, nullptr, topk, true)) != DSA_OK) return st;
+  if (T == 0) return DSA_OK;
+  if (!q_in || !k_in || !w) return fail(DSA_ERR_INVALID_ARGUMENT, "q_in, k_in and w are required");
+  if (!aligned(q_in, 16) || !aligned(k_in, 16) || !aligned(w, w_dtype == DSA_DTYPE_FP32 ? 4 : 2) ||
+      (q_op_out && !aligned(q_op_out, 16)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned input (q, k, q_op_out 16 B; weights 4 B)");
+  if ((st = check_outputs(out_indices, out_scores, out_lengths, nullptr, workspace)) != DSA_OK) return st;
+  const size_t need = dsa_index_forward_workspace_size(T, D, max_seqlen, precision);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  // workspace: score rows, then the quantised keys and their scales
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t es = precision == DSA_PREC_BF16 ? 2 : 1;
+  uint8_t* k_op = ws + up((size_t)T * (size_t)row_stride(max_seqlen) * sizeof(float));
+  uint8_t* k_scale = precision == DSA_PREC_BF16 ? nullptr : k_op + up((size_t)T * D * es);
+  // keys: LayerNorm, RoPE, quantisation
+  dsa::PreprocessLaunch pp;
+  pp.q_in = nullptr; pp.k_in = k_in; pp.in_bf16 = in_dtype == DSA_DTYPE_BF16;
+  pp.T = 0; pp.S = T; pp.H = H; pp.D = D;
+  pp.cu = cu_seqlens; pp.B = num_seqs;
+  pp.gamma = ln_gamma; pp.beta = ln_beta; pp.eps = ln_eps;
+  pp.cos_t = rope_cos; pp.sin_t = rope_sin;
+  pp.rope_dim = rope_dim; pp.max_pos = rope_max_pos; pp.interleaved = rope_interleaved ? 1 : 0;
+  pp.rope_fp32 = rope_fp32 ? 1 : 0; pp.precision = (int)precision;
+  pp.q_op = nullptr; pp.q_scale = nullptr; pp.k_op = k_op; pp.k_scale = k_scale;
+  pp.q_f32 = nullptr; pp.k_f32 = nullptr;
+  hipError_t e = dsa::launch_preprocess(pp, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_forward (keys)");
+  // scores with the query preprocessing fused into the scoring kernel, then top-k
+  dsa::ScoreTopkLaunch p = make_launch(nullptr, nullptr, k_op, k_scale, w, w_dtype, T, T, H, D, cu_seqlens,
+                                       num_seqs, max_seqlen, 1, nullptr, 0, topk, sm_scale, (int)precision,
+                                       out_indices, out_scores, out_lengths, nullptr, workspace);
+  set_fused_q(p, q_in, in_dtype, rope_cos, rope_sin, rope_dim, rope_max_pos, rope_interleaved, rope_fp32,
+              q_op_out, q_scale_out);
+  e = dsa::launch_score(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_forward (score)");
+  e = dsa::launch_topk(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_forward (top-k)");
+  return DSA_OK;
+}
+
 }  // extern "C"

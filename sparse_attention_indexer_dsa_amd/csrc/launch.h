@@ -44,7 +44,16 @@ struct ScoreTopkLaunch {
   float* scores;          // workspace: [T, stride] fp32
   int stride;             // row stride of the score workspace (floats)
   int max_cand;           // candidates per row upper bound
+  // Fused query preprocessing (q_in != nullptr): the scoring kernel builds its q operands
+  // from the raw queries (RoPE, carrier rounding, quantisation); q_op / q_scale unused.
+  const void* q_in = nullptr; bool in_bf16 = true;
+  const float* cos_t = nullptr; const float* sin_t = nullptr;
+  int rope_dim = 0, max_pos = 0, interleaved = 0, rope_fp32 = 0;
+  void* q_op_out = nullptr; uint8_t* q_scale_out = nullptr;   // optional copies of those operands
 };
+// Whether the fused query preprocessing supports this RoPE layout (rotate-half partners must
+// sit in the same lane of the MFMA operand layout).
+bool score_can_fuse_rope(int precision, int rope_dim, int interleaved);
 hipError_t launch_score(const ScoreTopkLaunch& p, hipStream_t st);
 hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st);
 

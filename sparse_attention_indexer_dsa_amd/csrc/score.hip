@@ -40,7 +40,12 @@ constexpr int kThreads = 256;
 struct ScoreArgs {
   const void* q_op; const uint8_t* q_scale;
   const void* k_op; const uint8_t* k_scale;
-  const void* w;
+  const void* w; int w_bf16;
+  // raw queries when the query preprocessing is done in this kernel (FUSE)
+  const void* q_in; int in_bf16;
+  const float* cos_t; const float* sin_t;
+  int R, max_pos, interleaved, rope_fp32;
+  void* q_op_out; uint8_t* q_scale_out;    // optional copies of the operands built (FUSE)
   int T, S, B, max_seqlen, kpool;
   const int32_t* cu; const int32_t* cu_pools;
   float sm_scale;
@@ -60,7 +65,185 @@ __device__ __forceinline__ float pair_sum(float x) {
   return u2f(r[0]) + u2f(r[1]);
 }
 
-template <int H, int D, int PREC, bool W_BF16>
+template <int PREC>
+using AOperand = typename std::conditional<PREC != kPrecBF16, i32x8, bf16x8>::type;
+
+// Query operands of one operand row built in registers from the raw query vector (fused
+// preprocessing): the same steps, in the same fp32 arithmetic, as the preprocessing kernel
+// (bf16 carrier rounding when rope_fp32 is off, RoPE, then bf16 RNE, or UE8M0 scale + E4M3
+// codes), but on the elements this lane holds in the MFMA A layout. The lane holds NG groups
+// of GS contiguous elements of the vector: fp8 group g = (kk, s) starts at 32 g + 16 hl
+// (GS = 16), bf16 group kk at 16 kk + 8 hl (GS = 8); the other half of the vector is in lane
+// l ^ 32. Rotate-half partners are in-lane (group g + half / GSTEP): the host takes the
+// fused path only when half is a multiple of GSTEP.
+template <int D, int PREC>
+__device__ __forceinline__ void build_q_row(const ScoreArgs& a, long long vec, bool ok, int pos, int hl,
+                                            AOperand<PREC> (&aop)[(PREC != kPrecBF16) ? D / 64 : D / 16],
+                                            int (&asc)[(PREC != kPrecBF16) ? D / 64 : D / 16]) {
+  constexpr bool kFP8 = PREC != kPrecBF16;
+  constexpr int GS = kFP8 ? 16 : 8;              // elements per group
+  constexpr int GSTEP = kFP8 ? 32 : 16;          // vector offset between consecutive groups
+  constexpr int NG = D / GSTEP;                  // groups per lane
+  constexpr int KSTEPS = kFP8 ? D / 64 : D / 16;
+  float x[NG][GS];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const long long off = vec * D + GSTEP * g + (GS)*hl;
+#pragma unroll
+    for (int c = 0; c < GS / 8; ++c) {
+      if (a.in_bf16) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (ok) raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q_in) + off + 8 * c);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[g][8 * c + 2 * j] = u2f(w4[j] << 16);
+          x[g][8 * c + 2 * j + 1] = u2f(w4[j] & 0xFFFF0000u);
+        }
+      } else {
+        float4 f0 = make_float4(0, 0, 0, 0), f1 = make_float4(0, 0, 0, 0);
+        if (ok) {
+          const float4* pf = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q_in) + off + 8 * c);
+          f0 = pf[0];
+          f1 = pf[1];
+        }
+        x[g][8 * c] = f0.x; x[g][8 * c + 1] = f0.y; x[g][8 * c + 2] = f0.z; x[g][8 * c + 3] = f0.w;
+        x[g][8 * c + 4] = f1.x; x[g][8 * c + 5] = f1.y; x[g][8 * c + 6] = f1.z; x[g][8 * c + 7] = f1.w;
+      }
+    }
+  }
+  if (!a.in_bf16 && !a.rope_fp32) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int j = 0; j < GS; ++j) x[g][j] = bf16_round(x[g][j]);
+  }
+  if (a.R > 0) {
+    const int rs = D - a.R, half = a.R / 2;
+    const float* crow = a.cos_t + (long long)min(pos, a.max_pos - 1) * half;
+    const float* srow = a.sin_t + (long long)min(pos, a.max_pos - 1) * half;
+    if (a.interleaved) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int j = 0; j < GS; j += 2) {
+          const int e = GSTEP * g + GS * hl + j;
+          if (e >= rs) {
+            const int cidx = (e - rs) / 2;
+            const float c = crow[cidx], sn = srow[cidx];
+            const float x1 = x[g][j], x2 = x[g][j + 1];
+            x[g][j] = x1 * c - x2 * sn;
+            x[g][j + 1] = x2 * c + x1 * sn;
+          }
+        }
+    } else {
+      const int dg = half / GSTEP;               // partner group distance
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int g2 = g + 1; g2 < NG; ++g2) {
+          const int e0 = GSTEP * g + GS * hl;    // first element of group g
+          if (g2 - g == dg && e0 >= rs && e0 < rs + half) {
+            const int cidx = e0 - rs;
+            float c[GS], sn[GS];
+#pragma unroll
+            for (int j = 0; j < GS; j += 4) {
+              const float4 cv = *reinterpret_cast<const float4*>(crow + cidx + j);
+              const float4 sv = *reinterpret_cast<const float4*>(srow + cidx + j);
+              c[j] = cv.x; c[j + 1] = cv.y; c[j + 2] = cv.z; c[j + 3] = cv.w;
+              sn[j] = sv.x; sn[j + 1] = sv.y; sn[j + 2] = sv.z; sn[j + 3] = sv.w;
+            }
+#pragma unroll
+            for (int j = 0; j < GS; ++j) {
+              const float x1 = x[g][j], x2 = x[g2][j];
+              x[g][j] = x1 * c[j] - x2 * sn[j];
+              x[g2][j] = x2 * c[j] + x1 * sn[j];
+            }
+          }
+        }
+    }
+    if (!a.rope_fp32) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int j = 0; j < GS; ++j) x[g][j] = bf16_round(x[g][j]);
+    }
+  }
+
+  if constexpr (!kFP8) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w4[j] = (uint32_t)f32_to_bf16_rne(x[kk][2 * j]) | ((uint32_t)f32_to_bf16_rne(x[kk][2 * j + 1]) << 16);
+      const uint4 v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      aop[kk] = *reinterpret_cast<const AOperand<PREC>*>(&v);
+      asc[kk] = 0;
+      if (a.q_op_out && ok)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op_out) + vec * D + GSTEP * kk + GS * hl) = v;
+    }
+  } else {
+
+  // E4M3 codes of a group at exponent e (x * 2^-e exact; the conversion rounds to nearest
+  // even, which matches the format definition for |values| <= 448)
+  auto encode = [&](int g, int e, uint32_t (&wd)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[g][4 * q], -e), ldexpf(x[g][4 * q + 1], -e), 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[g][4 * q + 2], -e), ldexpf(x[g][4 * q + 3], -e), v, true);
+      wd[q] = (uint32_t)v;
+    }
+  };
+  auto lane_pair_max = [](float m) {            // max over lanes l and l ^ 32 (non-negative)
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(m), f2u(m), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+  };
+  uint32_t wd[NG][4];
+  if (PREC == kPrecFP8) {
+    float amax = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int j = 0; j < GS; ++j) amax = fmaxf(amax, fabsf(x[g][j]));
+    const int e = ue8m0_exponent(lane_pair_max(amax));
+#pragma unroll
+    for (int g = 0; g < NG; ++g) encode(g, e, wd[g]);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) asc[kk] = e + 127;
+    if (a.q_scale_out && ok && hl == 0) a.q_scale_out[vec] = (uint8_t)(e + 127);
+  } else {
+    // group g = (kk, s) is half of 32-block 2 kk + s; lane hl supplies block 2 kk + hl's scale
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < GS; ++j) amax = fmaxf(amax, fabsf(x[g][j]));
+      const int e = ue8m0_exponent(lane_pair_max(amax));
+      encode(g, e, wd[g]);
+      if ((g & 1) == hl) {
+        asc[g / 2] = e + 127;
+        if (a.q_scale_out && ok) a.q_scale_out[vec * (D / 32) + g] = (uint8_t)(e + 127);
+      }
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    i32x8 t8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { t8[q] = (int)wd[2 * kk][q]; t8[4 + q] = (int)wd[2 * kk + 1][q]; }
+    aop[kk] = t8;
+  }
+  if (a.q_op_out && ok) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.q_op_out) + vec * D + GSTEP * g + GS * hl) =
+          make_uint4(wd[g][0], wd[g][1], wd[g][2], wd[g][3]);
+  }
+  }
+}
+
+template <int H, int D, int PREC, bool FUSE>
 __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
   constexpr bool kFP8 = PREC != kPrecBF16;
   constexpr int ES = kFP8 ? 1 : 2;               // operand bytes per element
@@ -96,10 +279,21 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 
   // ---- q operands, scales and weights of this wave's 64 rows (resident)
   const int ut0 = u0 + wv * TPW;                 // first token position of the wave
-  typedef typename std::conditional<kFP8, i32x8, bf16x8>::type AType;
+  typedef AOperand<PREC> AType;
   AType aop[2][KSTEPS];
   int asc[2][KSTEPS];
   float wl[2][16];
+  if (FUSE) {
+    // one operand row at a time (each holds 64 fp32 values while it is being built)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = rb * 32 + col;
+      const int tl = r / H, h = r % H;
+      __builtin_amdgcn_sched_barrier(0);
+      build_q_row<D, PREC>(a, (long long)(lo + ut0 + tl) * H + h, ut0 + tl < L, ut0 + tl, hl, aop[rb], asc[rb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int r = rb * 32 + col;                 // operand row held by this lane
@@ -107,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     const bool ok = ut0 + tl < L;
     const long long vec = (long long)(lo + ut0 + tl) * H + h;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
+    for (int kk = 0; kk < (FUSE ? 0 : KSTEPS); ++kk) {
       if (kFP8) {
         const uint8_t* base = reinterpret_cast<const uint8_t*>(a.q_op) + vec * D + kk * 64 + 16 * hl;
         uint4 v0 = ok ? *reinterpret_cast<const uint4*>(base) : make_uint4(0, 0, 0, 0);
@@ -133,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
       float wv_ = 0.f;
       if (ut0 + tl2 < L) {
         const long long wi = (long long)(lo + ut0 + tl2) * H + h2;
-        wv_ = W_BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.w)[wi]) : reinterpret_cast<const float*>(a.w)[wi];
+        wv_ = a.w_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.w)[wi]) : reinterpret_cast<const float*>(a.w)[wi];
       }
       wl[rb][i] = wv_;
     }
@@ -316,10 +510,10 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 }
 
 template <int H, int D, int PREC>
-hipError_t launch_h(const ScoreArgs& a, bool w_bf16, hipStream_t st) {
+hipError_t launch_h(const ScoreArgs& a, bool fuse, hipStream_t st) {
   const long long blocks = (long long)a.ntiles * a.B;
   if (blocks == 0) return hipSuccess;
-  if (w_bf16)
+  if (fuse)
     hipLaunchKernelGGL((score_kernel<H, D, PREC, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL((score_kernel<H, D, PREC, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
@@ -327,35 +521,45 @@ hipError_t launch_h(const ScoreArgs& a, bool w_bf16, hipStream_t st) {
 }
 
 template <int D, int PREC>
-hipError_t launch_d(const ScoreArgs& a, int H, bool w_bf16, hipStream_t st) {
+hipError_t launch_d(const ScoreArgs& a, int H, bool fuse, hipStream_t st) {
   switch (H) {
-    case 16: return launch_h<16, D, PREC>(a, w_bf16, st);
-    case 32: return launch_h<32, D, PREC>(a, w_bf16, st);
-    default: return launch_h<64, D, PREC>(a, w_bf16, st);
+    case 16: return launch_h<16, D, PREC>(a, fuse, st);
+    case 32: return launch_h<32, D, PREC>(a, fuse, st);
+    default: return launch_h<64, D, PREC>(a, fuse, st);
   }
 }
 
 template <int PREC>
-hipError_t launch_p(const ScoreArgs& a, int H, int D, bool w_bf16, hipStream_t st) {
-  return D == 128 ? launch_d<128, PREC>(a, H, w_bf16, st) : launch_d<64, PREC>(a, H, w_bf16, st);
+hipError_t launch_p(const ScoreArgs& a, int H, int D, bool fuse, hipStream_t st) {
+  return D == 128 ? launch_d<128, PREC>(a, H, fuse, st) : launch_d<64, PREC>(a, H, fuse, st);
 }
 
 }  // namespace
 
+bool score_can_fuse_rope(int precision, int rope_dim, int interleaved) {
+  if (rope_dim == 0 || interleaved) return true;
+  return (rope_dim / 2) % (precision == kPrecBF16 ? 16 : 32) == 0;
+}
+
 hipError_t launch_score(const ScoreTopkLaunch& p, hipStream_t st) {
   ScoreArgs a;
   a.q_op = p.q_op; a.q_scale = p.q_scale; a.k_op = p.k_op; a.k_scale = p.k_scale;
-  a.w = p.w;
+  a.w = p.w; a.w_bf16 = p.w_bf16;
+  a.q_in = p.q_in; a.in_bf16 = p.in_bf16;
+  a.cos_t = p.cos_t; a.sin_t = p.sin_t;
+  a.R = p.rope_dim; a.max_pos = p.max_pos; a.interleaved = p.interleaved; a.rope_fp32 = p.rope_fp32;
+  a.q_op_out = p.q_op_out; a.q_scale_out = p.q_scale_out;
   a.T = p.T; a.S = p.S; a.B = p.B; a.max_seqlen = p.max_seqlen; a.kpool = p.kpool;
   a.cu = p.cu; a.cu_pools = p.cu_pools;
   a.sm_scale = p.sm_scale;
   a.scores = p.scores; a.stride = p.stride; a.max_cand = p.max_cand;
   const int tq = 256 / p.H;
   a.ntiles = (p.max_seqlen + tq - 1) / tq;
+  const bool fuse = p.q_in != nullptr;
   switch (p.precision) {
-    case kPrecBF16: return launch_p<kPrecBF16>(a, p.H, p.D, p.w_bf16, st);
-    case kPrecFP8: return launch_p<kPrecFP8>(a, p.H, p.D, p.w_bf16, st);
-    default: return launch_p<kPrecMXFP8>(a, p.H, p.D, p.w_bf16, st);
+    case kPrecBF16: return launch_p<kPrecBF16>(a, p.H, p.D, fuse, st);
+    case kPrecFP8: return launch_p<kPrecFP8>(a, p.H, p.D, fuse, st);
+    default: return launch_p<kPrecMXFP8>(a, p.H, p.D, fuse, st);
   }
 }
 

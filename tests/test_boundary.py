@@ -22,6 +22,8 @@ def test_exports_every_declared_symbol(lib):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
     assert {"dsa_index_preprocess", "dsa_index_kpool", "dsa_index_workspace_size", "dsa_index_score_topk",
+            "dsa_index_score", "dsa_index_topk", "dsa_index_forward", "dsa_index_forward_workspace_size",
+            "dsa_index_score_fused",
             "dsa_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,6 +80,55 @@ def test_score_only_candidate_bound(lib):
     assert b"candidates per row" in lib.dsa_last_error()
     assert score(1 << 23, kpool=2) == 3         # 2^22 pools: only the workspace is missing
     assert score(1 << 20) == 3
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, dt=0, w=FAKE, wdt=1, T=64, H=64, D=128, cu=FAKE, B=1, maxlen=64, g=None, b=None,
+             eps=1e-6, cos=None, sin=None, R=0, maxpos=0, inter=0, f32=0, topk=8, sm=1.0, prec=1, oi=FAKE,
+             os=FAKE, ol=FAKE, qo=None, qs=None, ws=FAKE, wsb=10)
+    a.update(kw)
+    return lib.dsa_index_forward(a["q"], a["k"], a["dt"], a["w"], a["wdt"], a["T"], a["H"], a["D"], a["cu"], a["B"],
+                                 a["maxlen"], a["g"], a["b"], a["eps"], a["cos"], a["sin"], a["R"], a["maxpos"],
+                                 a["inter"], a["f32"], a["topk"], a["sm"], a["prec"], a["oi"], a["os"], a["ol"],
+                                 a["qo"], a["qs"], a["ws"], a["wsb"], None)
+
+
+def test_forward_validation(lib):
+    ws = lib.dsa_index_forward_workspace_size
+    # score rows, then keys and scales, each rounded up to 256 bytes, plus 256
+    assert ws(8192, 128, 4096, 1) == 8192 * 4096 * 4 + 8192 * 128 + 8192 + 256
+    assert ws(100, 64, 100, 0) == 100 * 128 * 4 + 12800 + 0 + 256
+    assert ws(100, 96, 100, 0) == 0
+    assert _fwd(lib, prec=3) == 2
+    assert _fwd(lib, H=48) == 2
+    assert _fwd(lib, R=32, cos=FAKE, sin=FAKE, maxpos=10) == 2          # fp8 rotate-half over 32 dims
+    assert b"rope_dim % 64" in lib.dsa_last_error()
+    assert _fwd(lib, R=32, cos=FAKE, sin=FAKE, maxpos=10, prec=0) == 3   # bf16 fuses it: only the workspace
+    assert _fwd(lib, R=32, cos=FAKE, sin=FAKE, maxpos=10, inter=1) == 3  # interleaved pairs are in-lane
+    assert _fwd(lib, topk=0) == 1
+    assert _fwd(lib, q=None) == 1
+    assert _fwd(lib, qo=FAKE + 4) == 1                                  # misaligned operand copy
+    assert _fwd(lib) == 3
+    assert b"workspace" in lib.dsa_last_error()
+    assert _fwd(lib, T=0) == 0
+
+
+def test_score_fused_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, dt=0, k=FAKE, ks=FAKE, w=FAKE, wdt=1, T=64, S=64, H=64, D=128, cu=FAKE, B=1, maxlen=64,
+                 cos=None, sin=None, R=0, maxpos=0, inter=0, f32=0, sm=1.0, prec=1, qo=None, qs=None, ws=FAKE,
+                 wsb=10)
+        a.update(kw)
+        return lib.dsa_index_score_fused(a["q"], a["dt"], a["k"], a["ks"], a["w"], a["wdt"], a["T"], a["S"], a["H"],
+                                         a["D"], a["cu"], a["B"], a["maxlen"], a["cos"], a["sin"], a["R"],
+                                         a["maxpos"], a["inter"], a["f32"], a["sm"], a["prec"], a["qo"], a["qs"],
+                                         a["ws"], a["wsb"], None)
+    assert call(dt=7) == 1
+    assert call(ks=None) == 1                                           # fp8 keys need scales
+    assert call(R=32, cos=FAKE, sin=FAKE, maxpos=10) == 2
+    assert call(R=64, cos=FAKE, sin=FAKE, maxpos=10) == 3               # all valid but the workspace
+    assert call(qo=FAKE + 2, wsb=1 << 30) == 1
+    assert call(T=0) == 0
 
 
 def _pre(lib, **kw):
