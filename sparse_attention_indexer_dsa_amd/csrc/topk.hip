@@ -300,33 +300,37 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   auto live = [&](int e) { return 4 * e * NT < cand; };
   auto idx = [&](int e, int j) { return 4 * (e * NT + tid) + j; };
   uint32_t key[EPT];
+  float val[EPT];                          // the scores themselves (finite; -0 folded to +0)
+  uint32_t kmax = 0, kmin1 = 0xFFFFFFFFu;  // kmin1 = min over candidates of (key - 1): no-candidate
+                                           // slots (key 0) wrap to the maximum and drop out
   {
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.scores + (long long)t * a.stride, cand * 4);
 #pragma unroll
     for (int e = 0; e < NCH; ++e) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) key[4 * e + j] = 0u;
+      for (int j = 0; j < 4; ++j) { key[4 * e + j] = 0u; val[4 * e + j] = 0.f; }
       if (live(e)) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rr, (e * NT + tid) * 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) key[4 * e + j] = idx(e, j) < cand ? score_key(u2f(v[j])) : 0u;
+        for (int j = 0; j < 4; ++j) {
+          const float x = u2f(v[j]) + 0.0f;      // -0 + 0 = +0
+          const uint32_t u = f2u(x);
+          // order-preserving key: negative scores invert all bits, others set the sign bit
+          const uint32_t k = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+          const uint32_t kk = idx(e, j) < cand ? k : 0u;
+          key[4 * e + j] = kk;
+          val[4 * e + j] = x;
+          kmax = kk > kmax ? kk : kmax;
+          kmin1 = (kk - 1u) < kmin1 ? (kk - 1u) : kmin1;
+        }
       }
     }
   }
 
   // ---- key range of the row's candidates (max and min in one reduction)
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int e = 0; e < NCH; ++e) {
-    if (live(e)) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t k = key[4 * e + j];
-        if (k != 0u) { kmax = k > kmax ? k : kmax; kmin = k < kmin ? k : kmin; }
-      }
-    }
-  }
+  uint32_t kmin = kmin1;
   block_minmax<NT>(kmin, kmax, wsum);
+  kmin += 1u;
 
   uint32_t thr = kmin;   // every selected key is >= thr
   int krem = 0;          // candidates equal to thr that are taken (lowest indices first)
@@ -339,10 +343,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     //      atomics rarely collide and the threshold bin holds few candidates.
     const float span = vmax - vmin;
     if (span > 0.f && span < INFINITY) {
+      // bin = (v - vmin) * 2048 / span as one fma (any rounding keeps the bins monotone in v)
       const float vscale = 2048.f / span;
+      const float voff = -vmin * vscale;
       int bin[EPT];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) bin[e] = key[e] != 0u ? min(2047, (int)((key_score(key[e]) - vmin) * vscale)) : -1;
+      for (int e = 0; e < EPT; ++e) {
+        const int bb = min(2047, max(0, (int)__builtin_fmaf(val[e], vscale, voff)));
+        bin[e] = key[e] != 0u ? bb : -1;
+      }
       for (int i = tid; i < 2048; i += NT) hist[i] = 0;
       if (tid == 0) misc[5] = 0;
       __syncthreads();
@@ -361,13 +370,29 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       if (c1 <= kValueList) {
         // the threshold bin's candidates to a list (order irrelevant), then one wave finds
         // the krem1-th largest among them by counting over lane values
+        {
+          int mine = 0;
 #pragma unroll
-        for (int e = 0; e < NCH; ++e)
-          if (live(e)) {
+          for (int e = 0; e < NCH; ++e)
+            if (live(e)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (bin[4 * e + j] == d1) aux[atomicAdd(&misc[5], 1)] = key[4 * e + j];
+              for (int j = 0; j < 4; ++j) mine += bin[4 * e + j] == d1;
+            }
+          const int incl = wave_prefix_sum(mine);
+          const int wtot = __builtin_amdgcn_readlane(incl, 63);
+          int base = 0;
+          if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&misc[5], wtot);
+          int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+          if (mine > 0) {
+#pragma unroll
+            for (int e = 0; e < NCH; ++e)
+              if (live(e)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  if (bin[4 * e + j] == d1) aux[pos++] = key[4 * e + j];
+              }
           }
+        }
         __syncthreads();
         if (tid < 64) {
           const uint32_t k = tid < c1 ? aux[tid] : 0u;
