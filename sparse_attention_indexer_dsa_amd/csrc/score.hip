@@ -65,6 +65,52 @@ __device__ __forceinline__ float pair_sum(float x) {
   return u2f(r[0]) + u2f(r[1]);
 }
 
+// Sum over the 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ int wave_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Query tile of block j. Tiles of all documents are taken in one order: tile index p
+// descending (longest causal rows first), documents ascending within a level, empty tiles
+// skipped. The hardware deals consecutive blocks to the XCDs in turn, so every XCD gets an
+// equal share of every length class (a block-to-document map by block index modulo the
+// document count would tie documents to XCDs). Up to 64 documents are handled this way (one
+// per lane; the search is a binary search on the number of tiles at level >= p); with more,
+// documents interleave by block index. Returns false for blocks past the last tile.
+__device__ __forceinline__ bool tile_of_block(const ScoreArgs& a, int tq, int j, int& b_out, int& p_out) {
+  if (a.B > 64) {
+    b_out = j % a.B;
+    p_out = a.ntiles - 1 - j / a.B;
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  int nt = 0;                                    // tiles of document `lane`
+  if (lane < a.B) {
+    const int lo = clampi(a.cu[lane], 0, a.T), hi = clampi(a.cu[lane + 1], lo, a.T);
+    nt = (min(hi - lo, a.max_seqlen) + tq - 1) / tq;
+  }
+  auto count_ge = [&](int p) { return wave_sum(max(0, nt - p)); };   // tiles with index >= p
+  if (count_ge(0) <= j) return false;
+  int plo = 0, phi = a.ntiles - 1;               // invariant: count_ge(plo) > j
+  while (plo < phi) {
+    const int mid = (plo + phi + 1) >> 1;
+    if (count_ge(mid) > j) plo = mid; else phi = mid - 1;
+  }
+  const int r = j - count_ge(plo + 1);           // rank among the documents with tile plo
+  const unsigned long long has = __ballot(nt > plo);
+  const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(has >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)has, 0));
+  const unsigned long long hit = __ballot(nt > plo && before == r);
+  b_out = __ffsll((long long)hit) - 1;
+  p_out = plo;
+  return true;
+}
+
 template <int PREC>
 using AOperand = typename std::conditional<PREC != kPrecBF16, i32x8, bf16x8>::type;
 
@@ -265,8 +311,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
   const int col = lane & 31;
 
   // ---- which document and query tile
-  const int b = blockIdx.x % a.B;
-  const int p = a.ntiles - 1 - blockIdx.x / a.B;
+  int b, p;
+  if (!tile_of_block(a, TQ, blockIdx.x, b, p)) return;
   const int lo = clampi(a.cu[b], 0, a.T);
   const int hi = clampi(a.cu[b + 1], lo, a.T);
   const int L = min(hi - lo, a.max_seqlen);
