@@ -15,6 +15,7 @@
 // tokens and the query's incomplete causal pool is appended when requested.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "device_common.h"
@@ -26,6 +27,7 @@ namespace {
 struct TopkArgs {
   const float* scores; int stride; int max_cand;
   int T, B, max_seqlen, kpool, kpool_tail, topk, p2max;
+  int hist_off;   // byte offset of the histogram in dynamic LDS
   const int32_t* cu; const int32_t* cu_pools;
   int32_t* out_indices; float* out_scores; int32_t* out_lengths; int32_t* out_pool_indices;
 };
@@ -255,9 +257,73 @@ __device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int krem, in
   __syncthreads();
 }
 
+// The same search over the 2048 pass-1 bins, which also stores above(d) for every bin in
+// starts[] (the first output slot of bin d) and sets misc[6] (zeroed by the caller) when a
+// thread owning a bin at or above the found one has a bin of more than `heavy` keys. Only
+// the thread whose bins hold the rank scans them one by one.
+template <int NT>
+__device__ __forceinline__ void scan_pass1_bins(const uint32_t* hist, int krem, int* wsum, int* misc,
+                                                uint32_t* starts, int heavy) {
+  constexpr int NW = NT / 64;
+  constexpr int PER = 2048 / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t h[PER];
+  if (PER >= 4) {
+#pragma unroll
+    for (int j = 0; j < PER; j += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(hist + tid * PER + j);
+      h[j] = q.x; h[j + 1] = q.y; h[j + 2] = q.z; h[j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) h[j] = hist[tid * PER + j];
+  }
+  int mine = 0;
+  uint32_t hmax = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { mine += (int)h[j]; hmax = max(hmax, h[j]); }
+  const int suf = wave_suffix_sum(mine);
+  if (lane == 0) wsum[wv] = suf;
+  __syncthreads();
+  int above = suf - mine;   // count in the bins of higher threads
+  if (NW > 1) {
+#pragma unroll
+    for (int w4 = 0; w4 < (NW + 3) / 4; ++w4) {
+      const int4 q = reinterpret_cast<const int4*>(wsum)[w4];
+      const int qa[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = 4 * w4 + j;
+        if (w < NW && w > wv) above += qa[j];
+      }
+    }
+  }
+  uint32_t st[PER];
+  st[PER - 1] = (uint32_t)above;
+#pragma unroll
+  for (int j = PER - 2; j >= 0; --j) st[j] = st[j + 1] + h[j + 1];
+  if (PER >= 4) {
+#pragma unroll
+    for (int j = 0; j < PER; j += 4)
+      *reinterpret_cast<uint4*>(starts + tid * PER + j) = make_uint4(st[j], st[j + 1], st[j + 2], st[j + 3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) starts[tid * PER + j] = st[j];
+  }
+  if (above < krem && hmax > (uint32_t)heavy) misc[6] = 1;
+  if (above < krem && krem <= above + mine) {
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      const int a0 = (int)st[j], hc = (int)h[j];
+      if (a0 < krem && krem <= a0 + hc) { misc[0] = tid * PER + j; misc[1] = a0; misc[2] = hc; }
+    }
+  }
+  __syncthreads();
+}
+
 constexpr int kValueList = 64;   // a threshold bin this small is resolved by counting
-constexpr int kBuckets = 1024;   // buckets of the ordering pass
-constexpr int kBucketMax = 64;   // larger buckets (heavy ties) fall back to the bitonic network
+constexpr int kBucketMax = 64;   // a selected pass-1 bin larger than this: bitonic ordering instead
+constexpr int kHistSlots = 2048 + 16;   // pass-1 bins, then a slot that counts non-candidates
 
 struct RowInfo {
   int t, b, lo, u, cand, nsel;
@@ -279,9 +345,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   u64* selA = reinterpret_cast<u64*>(smem);                                  // [p2max]
   u64* selB = selA + a.p2max;                                                // [p2max]
-  uint32_t* aux = reinterpret_cast<uint32_t*>(selB + a.p2max);               // [kBuckets]
-  uint32_t* hist = aux + kBuckets;                                           // [2048]
-  int* wsum = reinterpret_cast<int*>(hist + 2048);                           // [32]
+  uint32_t* bstart = reinterpret_cast<uint32_t*>(selB);                      // [2048], over selB
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);           // [kHistSlots]
+  int* wsum = reinterpret_cast<int*>(hist + kHistSlots);                     // [32]
   int* misc = wsum + 32;                                                     // [8]
 
   const int tid = threadIdx.x;
@@ -290,161 +356,294 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   const int t = blockIdx.x;
   const RowInfo cur = row_info(a, t);
   const int cand = cur.cand, nsel = cur.nsel;
+  const int lo = cur.lo, u = cur.u, b = cur.b;
 
   // ---- the row's scores as order-preserving keys (0: no candidate). Thread tid holds the
   //      4-candidate chunks c = e*NT + tid (candidates 4c .. 4c+3), so one load instruction
   //      covers 16*NT consecutive bytes, and a chunk group e lies entirely past the row once
   //      4*e*NT >= cand: such groups are skipped by every per-candidate pass (uniform branch).
+  //      All loads are issued before any is used; the buffer descriptor ends at the row's
+  //      last candidate, so loads of groups past it return zeros without touching memory.
   static_assert(EPT % 4 == 0, "candidates are held in chunks of 4");
+  static_assert(EPT <= 32, "one bit per candidate in a 32-bit mask");
   constexpr int NCH = EPT / 4;
   auto live = [&](int e) { return 4 * e * NT < cand; };
+  auto full = [&](int e) { return 4 * (e + 1) * NT <= cand; };
   auto idx = [&](int e, int j) { return 4 * (e * NT + tid) + j; };
-  uint32_t key[EPT];
+  uint32_t key[EPT];                       // defined for the chunk groups that are live
   float val[EPT];                          // the scores themselves (finite; -0 folded to +0)
-  uint32_t kmax = 0, kmin1 = 0xFFFFFFFFu;  // kmin1 = min over candidates of (key - 1): no-candidate
-                                           // slots (key 0) wrap to the maximum and drop out
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;   // over candidates only
   {
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.scores + (long long)t * a.stride, cand * 4);
+    __attribute__((ext_vector_type(4))) uint32_t raw[NCH];
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b128(rr, (e * NT + tid) * 16, 0, 0);
 #pragma unroll
     for (int e = 0; e < NCH; ++e) {
+      if (!live(e)) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { key[4 * e + j] = 0u; val[4 * e + j] = 0.f; }
-      if (live(e)) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rr, (e * NT + tid) * 16, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const float x = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
+        const uint32_t uu = f2u(x);
+        // order-preserving key: negative scores invert all bits, others set the sign bit
+        key[4 * e + j] = uu ^ ((uint32_t)((int)uu >> 31) | 0x80000000u);
+        val[4 * e + j] = x;
+      }
+      if (full(e)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float x = u2f(v[j]) + 0.0f;      // -0 + 0 = +0
-          const uint32_t u = f2u(x);
-          // order-preserving key: negative scores invert all bits, others set the sign bit
-          const uint32_t k = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
-          const uint32_t kk = idx(e, j) < cand ? k : 0u;
-          key[4 * e + j] = kk;
-          val[4 * e + j] = x;
-          kmax = kk > kmax ? kk : kmax;
-          kmin1 = (kk - 1u) < kmin1 ? (kk - 1u) : kmin1;
+          kmax = max(kmax, key[4 * e + j]);
+          kmin = min(kmin, key[4 * e + j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool in = idx(e, j) < cand;
+          key[4 * e + j] = in ? key[4 * e + j] : 0u;
+          kmax = max(kmax, key[4 * e + j]);
+          kmin = in ? min(kmin, key[4 * e + j]) : kmin;
         }
       }
     }
   }
 
   // ---- key range of the row's candidates (max and min in one reduction)
-  uint32_t kmin = kmin1;
   block_minmax<NT>(kmin, kmax, wsum);
-  kmin += 1u;
 
   uint32_t thr = kmin;   // every selected key is >= thr
-  int krem = 0;          // candidates equal to thr that are taken (lowest indices first)
+  int krem = cand;       // candidates equal to thr that are taken (lowest indices first)
+  int neq = 0;           // candidates equal to thr (known once the threshold is resolved)
+  bool resolved = cand <= topk;   // every candidate taken: no threshold needed
+  bool fast = false;     // order through the pass-1 bins (below)
+  int d1 = 0, a1 = 0;    // the threshold bin and the count of candidates in bins above it
   const float vmin = key_score(kmin), vmax = key_score(kmax);
-  if (cand > topk) {
-    krem = topk;
-    bool resolved = false;
+  const float span = vmax - vmin;
+  int bin[EPT];
+  if (span > 0.f && span < INFINITY) {
     // ---- pass 1: 2048 bins linear in the score over [vmin, vmax]. Bins are monotone in the
     //      score, and a smooth score distribution spreads evenly over them, so the LDS
-    //      atomics rarely collide and the threshold bin holds few candidates.
-    const float span = vmax - vmin;
-    if (span > 0.f && span < INFINITY) {
-      // bin = (v - vmin) * 2048 / span as one fma (any rounding keeps the bins monotone in v)
-      const float vscale = 2048.f / span;
-      const float voff = -vmin * vscale;
-      int bin[EPT];
+    //      atomics rarely collide and the threshold bin holds few candidates. The same bins
+    //      then order the selection: bins at and above the threshold bin, taken from the
+    //      top, are the selection in descending order up to the order inside each bin.
+    const float vscale = 2048.f / span;
+    const float voff = -vmin * vscale;
+    // bin = (v - vmin) * 2048 / span as one fma (any rounding keeps the bins monotone in v);
+    // non-candidates of the row's last chunk group count in slots 2048..2063 (spread over
+    // banks so that their atomics do not serialise on one address)
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int bb = min(2047, max(0, (int)__builtin_fmaf(val[e], vscale, voff)));
-        bin[e] = key[e] != 0u ? bb : -1;
+    for (int e = 0; e < NCH; ++e)
+      if (live(e)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int bb = min(2047, max(0, (int)__builtin_fmaf(val[4 * e + j], vscale, voff)));
+          bin[4 * e + j] = full(e) || key[4 * e + j] != 0u ? bb : 2048 + (tid & 15);
+        }
       }
-      for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-      if (tid == 0) misc[5] = 0;
+    for (int i = tid; i < kHistSlots / 4; i += NT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) { misc[5] = 0; misc[6] = 0; }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NCH; ++e)
+      if (live(e)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) atomicAdd(&hist[bin[4 * e + j]], 1u);
+      }
+    __syncthreads();
+    scan_pass1_bins<NT>(hist, nsel, wsum, misc, bstart, kBucketMax);
+    d1 = misc[0];
+    a1 = misc[1];
+    const int c1 = misc[2];
+    const bool heavy = misc[6] != 0;
+    if (cand > topk && c1 <= kValueList) {
+      const int krem1 = topk - a1;
+      // the threshold bin's candidates to a list (order irrelevant), then one wave finds
+      // the krem1-th largest among them by counting over lane values
+      uint32_t* list = reinterpret_cast<uint32_t*>(selA);
+      {
+        int mine = 0;
+#pragma unroll
+        for (int e = 0; e < NCH; ++e)
+          if (live(e)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mine += bin[4 * e + j] == d1;
+          }
+        const int incl = wave_prefix_sum(mine);
+        const int wtot = __builtin_amdgcn_readlane(incl, 63);
+        int base = 0;
+        if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&misc[5], wtot);
+        int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+        if (mine > 0) {
+#pragma unroll
+          for (int e = 0; e < NCH; ++e)
+            if (live(e)) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (bin[4 * e + j] == d1) list[pos++] = key[4 * e + j];
+            }
+        }
+      }
       __syncthreads();
+      if (tid < 64) {
+        const uint32_t k = tid < c1 ? list[tid] : 0u;
+        int gt = 0, ge = 0;
+        for (int q = 0; q < c1; ++q) {
+          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)k, q);
+          gt += o > k;
+          ge += o >= k;
+        }
+        const bool hit = tid < c1 && gt < krem1 && krem1 <= ge;
+        const u64 m = __ballot(hit);
+        const int src = __ffsll((long long)m) - 1;
+        const uint32_t fk = __shfl(k, src, 64);
+        const int fg = __shfl(gt, src, 64);
+        const int fe = __shfl(ge, src, 64);
+        if (tid == 0) { misc[3] = (int)fk; misc[4] = krem1 - fg; misc[7] = fe - fg; }
+      }
+      __syncthreads();
+      thr = (uint32_t)misc[3];
+      krem = misc[4];
+      neq = misc[7];
+      resolved = true;
+    }
+    fast = resolved && !heavy;
+  }
+
+  if (fast) {
+    // ---- selection straight into bin order: bins hold their candidates from bstart[d]
+    //      (the count in bins above d) on. Keys above thr are all taken; of the keys equal to
+    //      thr (all in bin d1) the krem lowest indices, which needs their index order only
+    //      when fewer are taken than exist.
+    uint32_t eqtake = 0xFFFFFFFFu;   // bit 4e+j: a key equal to thr that is taken
+    if (neq > krem) {
+      // group e's equal keys come after all equal keys of groups < e; inside group e, thread
+      // order then position in the chunk. Fields of 16 bits, two groups per prefix sum.
+      eqtake = 0u;
+      int eq_before_group = 0;
+#pragma unroll
+      for (int e2 = 0; e2 < NCH; e2 += 2) {
+        int c0 = 0, c1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (live(e2)) c0 += key[4 * e2 + j] == thr;
+          if (e2 + 1 < NCH && live(e2 + 1)) c1 += key[4 * (e2 + 1) + j] == thr;
+        }
+        int gtot;
+        const int gb = block_exclusive_sum<NT>((c1 << 16) | c0, wsum, gtot);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = e2 + h;
+          if (e < NCH && live(e)) {
+            int rank = eq_before_group + (h ? gb >> 16 : gb & 0xFFFF);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (key[4 * e + j] == thr) {
+                if (rank < krem) eqtake |= 1u << (4 * e + j);
+                ++rank;
+              }
+            eq_before_group += h ? gtot >> 16 : gtot & 0xFFFF;
+          }
+        }
+      }
+    }
+    // Selected entries as (~key, bin, index) packed so that ascending order within a bin is
+    // (score descending, index ascending); indices are < 2^16 and bins < 2^11.
+    u64* ord = selA;
+    auto put = [&](int e, int j) {
+      const uint32_t k = key[4 * e + j];
+      const uint32_t d = (uint32_t)bin[4 * e + j];
+      const uint32_t slot = atomicAdd(&bstart[d], 1u);
+      ord[slot] = ((u64)(~k) << 32) | (d << 16) | (uint32_t)idx(e, j);
+    };
+    if (neq > krem) {
+#pragma unroll
+      for (int e = 0; e < NCH; ++e)
+        if (live(e)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t k = key[4 * e + j];
+            if (k > thr || (k == thr && ((eqtake >> (4 * e + j)) & 1u))) put(e, j);
+          }
+        }
+    } else {
 #pragma unroll
       for (int e = 0; e < NCH; ++e)
         if (live(e)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (bin[4 * e + j] >= 0) atomicAdd(&hist[bin[4 * e + j]], 1u);
+            if (key[4 * e + j] >= thr) put(e, j);
+        }
+    }
+    __syncthreads();
+    // ---- each entry's rank inside its bin gives its output position. After the scatter
+    //      bstart[d] is the end of bin d; bins above d1 are taken whole, bin d1 from a1 on.
+    float* os = a.out_scores + (long long)t * topk;
+    const int width = kp == 1 ? topk : topk * kp + kp - 1;
+    int32_t* oi = a.out_indices + (long long)t * width;
+    int32_t* op = (kp > 1 && a.out_pool_indices) ? a.out_pool_indices + (long long)t * topk : nullptr;
+    const int pbase = kp > 1 ? a.cu_pools[b] : 0;
+    for (int i = tid; i < nsel; i += NT) {
+      const u64 v = ord[i];
+      const uint32_t lw = (uint32_t)v;
+      const int d = (int)((lw >> 16) & 2047u);
+      const int end = (int)bstart[d];
+      const int s0 = d == d1 ? a1 : end - (int)hist[d];
+      int r = 0;
+      for (int q = s0; q < end; ++q) r += ord[q] < v;
+      const int dest = s0 + r;
+      const int ix = (int)(lw & 0xFFFFu);
+      os[dest] = key_score(~(uint32_t)(v >> 32));
+      if (kp == 1) {
+        oi[dest] = lo + ix;
+      } else {
+        if (op) op[dest] = pbase + ix;
+        for (int j = 0; j < kp; ++j) oi[dest * kp + j] = lo + ix * kp + j;
+      }
+    }
+    for (int j = nsel + tid; j < topk; j += NT) os[j] = -INFINITY;
+    if (kp == 1) {
+      for (int j = nsel + tid; j < topk; j += NT) oi[j] = -1;
+      if (tid == 0) a.out_lengths[t] = nsel;
+    } else {
+      if (op)
+        for (int j = nsel + tid; j < topk; j += NT) op[j] = -1;
+      const int tail = a.kpool_tail ? (u + 1) % kp : 0;
+      const int npool_tok = nsel * kp;
+      const int tail_start = lo + (u / kp) * kp;
+      for (int s2 = npool_tok + tid; s2 < width; s2 += NT)
+        oi[s2] = s2 < npool_tok + tail ? tail_start + (s2 - npool_tok) : -1;
+      if (tid == 0) a.out_lengths[t] = npool_tok + tail;
+    }
+    return;
+  }
+
+  if (!resolved) {
+    // ---- clustered rows (or no usable score range): radix select on the key bits
+    //      (11 + 11 + 10)
+    uint32_t prefix = 0, pmask = 0;
+    krem = topk;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nbins = pass == 2 ? 1024 : 2048;
+      __syncthreads();
+      for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < NCH; ++e)
+        if (live(e)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t k = key[4 * e + j];
+            if (k != 0u && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+          }
         }
       __syncthreads();
       find_rank_bin<NT, 2048>(hist, krem, wsum, misc);
-      const int d1 = misc[0];
-      const int c1 = misc[2];
-      const int krem1 = krem - misc[1];
-      if (c1 <= kValueList) {
-        // the threshold bin's candidates to a list (order irrelevant), then one wave finds
-        // the krem1-th largest among them by counting over lane values
-        {
-          int mine = 0;
-#pragma unroll
-          for (int e = 0; e < NCH; ++e)
-            if (live(e)) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) mine += bin[4 * e + j] == d1;
-            }
-          const int incl = wave_prefix_sum(mine);
-          const int wtot = __builtin_amdgcn_readlane(incl, 63);
-          int base = 0;
-          if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&misc[5], wtot);
-          int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
-          if (mine > 0) {
-#pragma unroll
-            for (int e = 0; e < NCH; ++e)
-              if (live(e)) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  if (bin[4 * e + j] == d1) aux[pos++] = key[4 * e + j];
-              }
-          }
-        }
-        __syncthreads();
-        if (tid < 64) {
-          const uint32_t k = tid < c1 ? aux[tid] : 0u;
-          int gt = 0, ge = 0;
-          for (int q = 0; q < c1; ++q) {
-            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)k, q);
-            gt += o > k;
-            ge += o >= k;
-          }
-          const bool hit = tid < c1 && gt < krem1 && krem1 <= ge;
-          const u64 m = __ballot(hit);
-          const int src = __ffsll((long long)m) - 1;
-          const uint32_t fk = __shfl(k, src, 64);
-          const int fg = __shfl(gt, src, 64);
-          if (tid == 0) { misc[3] = (int)fk; misc[4] = krem1 - fg; }
-        }
-        __syncthreads();
-        thr = (uint32_t)misc[3];
-        krem = misc[4];
-        resolved = true;
-      }
+      krem -= misc[1];
+      prefix |= (uint32_t)misc[0] << shift;
+      pmask |= (uint32_t)(nbins - 1) << shift;
     }
-    if (!resolved) {
-      // ---- clustered rows: radix select on the key bits (11 + 11 + 10)
-      uint32_t prefix = 0, pmask = 0;
-      krem = topk;
-#pragma unroll 1
-      for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nbins = pass == 2 ? 1024 : 2048;
-        __syncthreads();
-        for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < NCH; ++e)
-          if (live(e)) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t k = key[4 * e + j];
-              if (k != 0u && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
-            }
-          }
-        __syncthreads();
-        find_rank_bin<NT, 2048>(hist, krem, wsum, misc);
-        krem -= misc[1];
-        prefix |= (uint32_t)misc[0] << shift;
-        pmask |= (uint32_t)(nbins - 1) << shift;
-      }
-      thr = prefix;
-    }
-  } else {
-    krem = cand;   // every candidate is taken
+    thr = prefix;
   }
 
   // ---- compaction into selB[0, nsel): keys above thr (in any order: the ordering pass
@@ -465,9 +664,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
   int tot;
   const int before = block_exclusive_sum<NT>((n_gt << 16) | n_eq, wsum, tot);
-  const int ngt = tot >> 16, neq = tot & 0xFFFF;
+  const int ngt = tot >> 16, neq_all = tot & 0xFFFF;
   int pos_gt = before >> 16;
-  if (neq <= krem) {
+  if (neq_all <= krem) {
     int pos_eq = ngt + (before & 0xFFFF);
 #pragma unroll
     for (int e = 0; e < NCH; ++e)
@@ -489,9 +688,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       int c0 = 0, c1 = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t k0 = key[4 * e2 + j];
-        c0 += k0 == thr && k0 != 0u;
-        if (e2 + 1 < NCH) {
+        if (live(e2)) {
+          const uint32_t k0 = key[4 * e2 + j];
+          c0 += k0 == thr && k0 != 0u;
+        }
+        if (e2 + 1 < NCH && live(e2 + 1)) {
           const uint32_t k1 = key[4 * (e2 + 1) + j];
           c1 += k1 == thr && k1 != 0u;
         }
@@ -501,7 +702,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int e = e2 + h;
-        if (e < NCH) {
+        if (e < NCH && live(e)) {
           int rank = eq_before_group + ((h ? gb >> 16 : gb & 0xFFFF));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -526,93 +727,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       }
   }
 
-  // ---- ordering of selB[0, nsel): bucket b = floor((vmax - score) * scale) over
-  //      [score(thr), vmax] (ascending b = descending score); counts, starts by a prefix
-  //      sum, scatter, then each entry's exact rank inside its bucket
-  const float vthr = key_score(thr);
-  const float ospan = vmax - vthr;
-  const float oscale = (ospan > 0.f && ospan < INFINITY) ? (float)(kBuckets - 1) / ospan : 0.f;
-  constexpr int SPT = 8;                   // selected entries per thread handled in registers
-  uint32_t* cnt = hist;                    // [kBuckets]
-  uint32_t* start = hist + kBuckets;       // [kBuckets]
-  uint32_t* fill = aux;                    // [kBuckets]
-  for (int i = tid; i < kBuckets; i += NT) cnt[i] = 0;
-  __syncthreads();
-  u64 mine_v[SPT];
-  int mine_b[SPT];
-  const int nmine = (nsel - tid + NT - 1) / NT;   // entries tid, tid + NT, ...
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int i = tid + j * NT;
-    mine_b[j] = -1;
-    if (j < nmine) {
-      mine_v[j] = selB[i];
-      mine_b[j] = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(mine_v[j] >> 32))) * oscale));
-      atomicAdd(&cnt[mine_b[j]], 1u);
-    }
-  }
-  for (int i = tid + SPT * NT; i < nsel; i += NT) {      // beyond the register share
-    const int bk = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(selB[i] >> 32))) * oscale));
-    atomicAdd(&cnt[bk], 1u);
-  }
-  __syncthreads();
-  {
-    constexpr int PER = kBuckets / NT > 0 ? kBuckets / NT : 1;
-    uint32_t c[PER];
-    int m = 0, big = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int bk = tid * PER + j;
-      c[j] = bk < kBuckets ? cnt[bk] : 0u;
-      m += (int)c[j];
-      big |= c[j] > (uint32_t)kBucketMax;
-    }
-    int btot;
-    int run = block_exclusive_sum<NT>(m, wsum, btot);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int bk = tid * PER + j;
-      if (bk < kBuckets) { start[bk] = run; fill[bk] = run; run += (int)c[j]; }
-    }
-    if (tid == 0) misc[2] = 0;
-    __syncthreads();
-    if (big) misc[2] = 1;
-  }
-  __syncthreads();
-  u64* tmp = selA;
-  const bool heavy = misc[2] != 0;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j)
-    if (mine_b[j] >= 0) tmp[atomicAdd(&fill[mine_b[j]], 1u)] = mine_v[j];
-  for (int i = tid + SPT * NT; i < nsel; i += NT) {
-    const u64 v = selB[i];
-    const int bk = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(v >> 32))) * oscale));
-    tmp[atomicAdd(&fill[bk], 1u)] = v;
-  }
-  __syncthreads();
+  // ---- ordering of selB[0, nsel) by the bitonic network: rows that come here have scores
+  //      that the linear bins do not separate (ties, clusters, no finite range)
   int n2 = 64;
   while (n2 < nsel) n2 <<= 1;
-  if (heavy) {
-    // heavy ties / clustering: the bitonic network on the whole selection
-    for (int i = nsel + tid; i < n2; i += NT) tmp[i] = ~0ull;
-    __syncthreads();
-    if (n2 <= 128) bitonic_sort<1, NT>(tmp, n2);
-    else bitonic_sort<4, NT>(tmp, n2);
-  } else {
-    for (int i = tid; i < nsel; i += NT) {
-      const u64 v = tmp[i];
-      const int bk = min(kBuckets - 1, (int)((vmax - key_score(~(uint32_t)(v >> 32))) * oscale));
-      const int s0 = start[bk], n = cnt[bk];
-      int r = 0;
-      for (int q = 0; q < n; ++q) r += tmp[s0 + q] < v;
-      selB[s0 + r] = v;
-    }
-    __syncthreads();
-  }
-  const u64* sel = heavy ? tmp : selB;
+  for (int i = nsel + tid; i < n2; i += NT) selB[i] = ~0ull;
+  __syncthreads();
+  if (n2 <= 128) bitonic_sort<1, NT>(selB, n2);
+  else bitonic_sort<4, NT>(selB, n2);
+  const u64* sel = selB;
 
   // ---- outputs
-  const int lo = cur.lo, u = cur.u, b = cur.b;
   float* os = a.out_scores + (long long)t * topk;
   for (int j = tid; j < topk; j += NT)
     os[j] = j < nsel ? key_score(~(uint32_t)(sel[j] >> 32)) : -INFINITY;
@@ -672,8 +797,15 @@ int p2_of(int topk, int max_cand) {
 
 }  // namespace
 
+// Dynamic LDS layout: selA [p2max] u64 | selB [p2max] u64 in a region of at least 2048 u32
+// (the pass-1 bin starts overlay it) | hist [kHistSlots] u32 | wsum [32] | misc [8].
+int topk_hist_offset(int max_cand, int topk) {
+  const int p2 = p2_of(topk, max_cand);
+  return p2 * 8 + std::max(p2 * 8, 2048 * 4);
+}
+
 size_t topk_lds_bytes(int max_cand, int topk) {
-  return (size_t)p2_of(topk, max_cand) * 8 * 2 + (size_t)kBuckets * 4 + 2048 * 4 + 32 * 4 + 8 * 4;
+  return (size_t)topk_hist_offset(max_cand, topk) + kHistSlots * 4 + 32 * 4 + 8 * 4;
 }
 
 hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
@@ -683,6 +815,7 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
   a.T = p.T; a.B = p.B; a.max_seqlen = p.max_seqlen; a.kpool = p.kpool; a.kpool_tail = p.kpool_tail;
   a.topk = p.topk;
   a.p2max = p2_of(p.topk, p.max_cand);
+  a.hist_off = topk_hist_offset(p.max_cand, p.topk);
   a.cu = p.cu; a.cu_pools = p.cu_pools;
   a.out_indices = p.out_indices; a.out_scores = p.out_scores; a.out_lengths = p.out_lengths;
   a.out_pool_indices = p.out_pool_indices;

@@ -1,0 +1,124 @@
+"""Selection kernel on crafted score rows (GPU), against the oracle's row selection.
+
+The workspace rows are written directly, so every row's scores are exact fp32 values and
+the selection must match the oracle exactly: the same local indices in the same order
+(score descending, index ascending; -0 counts as +0), the scores themselves, -1 / -inf
+padding and the lengths. Row patterns reach every branch of the kernel: smooth rows (bin
+ordering), ties at the threshold with fewer taken than exist, a bin above the threshold
+holding more than its ordering limit, a clustered threshold bin (radix select), an outlier
+that crushes the linear bins, constant rows, small integers (ties everywhere), signed
+zeros, negative rows and magnitudes from subnormal to 1e30. Document lengths select each
+of the launch shapes (up to 1024, 2048, 4096, 8192, 16384 and 32768 candidates per row).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+NPAT = 10
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import sparse_attention_indexer_dsa_amd as dsa
+    dsa.load()
+
+
+def _row(p, cand, topk, rng):
+    """Scores of one row with pattern p (fp32)."""
+    v = (rng.standard_normal(cand) * 3.0).astype(np.float32)
+    k = min(topk, cand)
+    desc = np.sort(v)[::-1]
+    if p == 1:      # ties straddling the threshold: fewer taken than equal
+        v[rng.choice(cand, size=min(cand, 20), replace=False)] = desc[k - 1]
+    elif p == 2:    # one bin above the threshold holding many equal keys
+        v[rng.choice(cand, size=min(cand, 100), replace=False)] = desc[k // 4]
+    elif p == 3:    # a clustered threshold
+        v[rng.choice(cand, size=min(cand, 300), replace=False)] = desc[k - 1]
+    elif p == 4:    # one outlier
+        v[rng.integers(cand)] = np.float32(1e30)
+    elif p == 5:    # constant
+        v[:] = np.float32(1.25)
+    elif p == 6:    # small integers
+        v = rng.integers(0, 8, cand).astype(np.float32)
+    elif p == 7:    # signed zeros with a few nonzero scores
+        v = np.where(rng.random(cand) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        m = rng.random(cand) < 0.1
+        v[m] = rng.standard_normal(int(m.sum())).astype(np.float32)
+    elif p == 8:    # all negative
+        v = -np.abs(v) - np.float32(1.0)
+    elif p == 9:    # magnitudes from subnormal to 1e30
+        v = (rng.standard_normal(cand) * 10.0 ** rng.integers(-44, 31, cand)).astype(np.float32)
+    return v
+
+
+def _sample_rows(L, topk, rng):
+    rows = set(range(max(0, L - 12), L))
+    rows |= {t for t in (0, 1, 2, 63, 64, 65, topk - 2, topk - 1, topk, topk + 1) if 0 <= t < L}
+    rows |= set(int(x) for x in rng.choice(L, size=min(L, 40), replace=False))
+    return sorted(rows)
+
+
+def _run(L, topk, kp, tail, seed):
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    rng = np.random.default_rng(seed)
+    max_cand = L if kp == 1 else L // kp
+    stride = (max(1, max_cand) + 63) // 64 * 64
+    gen_t = torch.Generator(device="cuda").manual_seed(seed)
+    flat = torch.randn(L * stride + 64, generator=gen_t, device="cuda", dtype=torch.float32) * 3.0
+    ws = flat[:L * stride].view(L, stride)     # the library asks for 256 bytes beyond the rows
+    rows = _sample_rows(L, topk, rng)
+    want = {}
+    for i, t in enumerate(rows):
+        cand = (t + 1) // kp
+        if cand == 0:
+            continue
+        v = _row(i % NPAT, cand, topk, rng)
+        ws[t, :cand] = torch.from_numpy(v).cuda()
+        want[t] = v
+    # rows left random are checked too: read back after the call
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    cu_pools = torch.tensor([0, L // kp], dtype=torch.int32, device="cuda") if kp > 1 else None
+    out = dsa.topk(flat, L, cu, L, topk, kpool=kp, cu_pools=cu_pools, kpool_tail=tail)
+    torch.cuda.synchronize()
+    extra = [int(x) for x in rng.choice(L, size=min(L, 16), replace=False)]
+    host = {n: out[n].cpu().numpy() for n in out}
+    for t in sorted(set(want) | set(extra)):
+        cand = (t + 1) // kp
+        v = want[t] if t in want else ws[t, :cand].cpu().numpy()
+        sel, s = orc.topk_row(v.astype(np.float64), topk)
+        n = sel.size
+        sc = host["scores"][t]
+        assert np.array_equal(sc[:n].astype(np.float64), s), (t, sc[:8], s[:8])
+        assert np.all(np.isneginf(sc[n:])), t
+        if kp == 1:
+            idx = host["indices"][t].astype(np.int64)
+            assert host["lengths"][t] == n, (t, host["lengths"][t], n)
+            assert np.array_equal(idx[:n], sel), (t, idx[:8], sel[:8])
+            assert np.all(idx[n:] == -1), t
+        else:
+            pidx = host["pool_indices"][t].astype(np.int64)
+            assert np.array_equal(pidx[:n], sel), (t, pidx[:8], sel[:8])
+            assert np.all(pidx[n:] == -1), t
+            toks = orc.expand(sel, t, kp, 0, tail)
+            tok = host["indices"][t].astype(np.int64)
+            assert host["lengths"][t] == toks.size, t
+            assert np.array_equal(tok[:toks.size], toks), t
+            assert np.all(tok[toks.size:] == -1), t
+
+
+@pytest.mark.parametrize("L, topk", [(1000, 64), (2000, 256), (3000, 7), (4000, 512), (8000, 2048),
+                                     (16000, 2048), (32768, 2048), (1500, 2048)])
+def test_selection_patterns(L, topk):
+    _run(L, topk, 1, True, L + topk)
+
+
+@pytest.mark.parametrize("tail", [True, False])
+def test_selection_patterns_kpool(tail):
+    _run(8000, 512, 4, tail, 11 + tail)
