@@ -2,17 +2,18 @@
 //
 // One workgroup per query row. Each thread holds 4-candidate chunks of the row, interleaved
 // across the workgroup, as order-preserving uint32 keys in registers; chunk groups past the
-// row's last candidate are skipped by every pass. The topk-th largest key comes from a
-// 2048-bin histogram linear in the score (LDS integer atomics; the threshold bin's few keys
-// are then ranked exactly), or for clustered rows from an 11 + 11 + 10-bit radix select.
-// Every candidate above it is taken and, among candidates equal to it, the lowest indices
-// (deterministic tie breaking, Megatron-LM PR 5992, "Key changes"). Slots in the selection
-// buffer come from block prefix sums, so the kernel uses no floating-point atomics and its
-// result does not depend on scheduling. The selection is ordered by (score descending,
-// index ascending): buckets linear in the score, a prefix sum, a scatter and an exact rank
-// inside each bucket, or a bitonic network when a bucket is heavy (ties). Outputs are
-// padded with -1 / -inf. For KPool (PR 7522, "Changes") selected pools are expanded to their
-// tokens and the query's incomplete causal pool is appended when requested.
+// row's last candidate are skipped by every pass. A 2048-bin histogram linear in the score
+// (LDS integer atomics) gives the bin holding the topk-th largest key, whose few keys are
+// then ranked exactly. Every candidate above that key is taken and, among candidates equal
+// to it, the lowest indices (deterministic tie breaking, Megatron-LM PR 5992, "Key
+// changes"). The same bins order the selection: bin starts come from the histogram's suffix
+// sums, every selected candidate goes to its bin's range, and its exact rank inside the bin
+// (score descending, index ascending) gives its output position. Rows whose bins do not
+// separate the scores (clustered or tied scores, outliers, no finite range) take an
+// 11 + 11 + 10-bit radix select, a compaction by block prefix sums and a bitonic network.
+// The kernel uses no floating-point atomics and its result does not depend on scheduling.
+// Outputs are padded with -1 / -inf. For KPool (PR 7522, "Changes") selected pools are
+// expanded to their tokens and the query's incomplete causal pool is appended when requested.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
