@@ -29,6 +29,9 @@ struct TopkArgs {
   const float* scores; int stride; int max_cand;
   int T, B, max_seqlen, kpool, kpool_tail, topk, p2max;
   int hist_off;   // byte offset of the histogram in dynamic LDS
+  // Rows handled by this launch: those with a candidate count in [cls_lo, cls_hi], in
+  // document order; cls_map == 0: every row, block b = row b.
+  int cls_lo, cls_hi, cls_map;
   const int32_t* cu; const int32_t* cu_pools;
   int32_t* out_indices; float* out_scores; int32_t* out_lengths; int32_t* out_pool_indices;
 };
@@ -258,13 +261,13 @@ __device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int krem, in
   __syncthreads();
 }
 
-// The same search over the 2048 pass-1 bins, which also stores above(d) for every bin in
-// starts[] (the first output slot of bin d) and sets misc[6] (zeroed by the caller) when a
-// thread owning a bin at or above the found one has a bin of more than `heavy` keys. Only
-// the thread whose bins hold the rank scans them one by one.
+// The same search over the 2048 pass-1 bins, which then replaces every bin's count c by
+// (above(d) << 16) | c: above(d) is the first output slot of bin d (counts and slots are at
+// most 32768, so both fields fit). Sets misc[6] (zeroed by the caller) when a thread owning
+// a bin at or above the found one has a bin of more than `heavy` keys. Only the thread whose
+// bins hold the rank scans them one by one.
 template <int NT>
-__device__ __forceinline__ void scan_pass1_bins(const uint32_t* hist, int krem, int* wsum, int* misc,
-                                                uint32_t* starts, int heavy) {
+__device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* wsum, int* misc, int heavy) {
   constexpr int NW = NT / 64;
   constexpr int PER = 2048 / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -306,10 +309,11 @@ __device__ __forceinline__ void scan_pass1_bins(const uint32_t* hist, int krem, 
   if (PER >= 4) {
 #pragma unroll
     for (int j = 0; j < PER; j += 4)
-      *reinterpret_cast<uint4*>(starts + tid * PER + j) = make_uint4(st[j], st[j + 1], st[j + 2], st[j + 3]);
+      *reinterpret_cast<uint4*>(hist + tid * PER + j) =
+          make_uint4(st[j] << 16 | h[j], st[j + 1] << 16 | h[j + 1], st[j + 2] << 16 | h[j + 2], st[j + 3] << 16 | h[j + 3]);
   } else {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) starts[tid * PER + j] = st[j];
+    for (int j = 0; j < PER; ++j) hist[tid * PER + j] = st[j] << 16 | h[j];
   }
   if (above < krem && hmax > (uint32_t)heavy) misc[6] = 1;
   if (above < krem && krem <= above + mine) {
@@ -341,12 +345,43 @@ __device__ __forceinline__ RowInfo row_info(const TopkArgs& a, int t) {
   return r;
 }
 
+// Row of block j among the rows whose candidate count lies in [cls_lo, cls_hi] (documents in
+// order, positions ascending); false when j is past them. Candidate counts grow with the
+// position u in a document, so each document contributes the positions [ulo, uhi]; the
+// class holding max_cand also takes every position past it. One lane per document, 64
+// documents per step; every wave computes the same result.
+__device__ bool class_row(const TopkArgs& a, int j, int& t) {
+  const int lane = threadIdx.x & 63;
+  const int kp = a.kpool;
+  const int ulo = a.cls_lo <= 0 ? 0 : a.cls_lo * kp - 1;
+  const int uhi = a.cls_hi >= a.max_cand ? 0x7FFFFFFF : a.cls_hi * kp + kp - 2;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    int n = 0, lo = 0;
+    if (b < a.B) {
+      lo = clampi(a.cu[b], 0, a.T);
+      const int hi = clampi(a.cu[b + 1], lo, a.T);
+      n = max(0, min(hi - lo - 1, uhi) - ulo + 1);
+    }
+    const int incl = wave_prefix_sum(n);
+    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    const int r = j - base;
+    if (r < tot) {
+      const u64 hit = __ballot(incl - n <= r && r < incl);
+      const int src = __ffsll((long long)hit) - 1;
+      t = __shfl(lo, src, 64) + ulo + (r - __shfl(incl - n, src, 64));
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
+
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   u64* selA = reinterpret_cast<u64*>(smem);                                  // [p2max]
-  u64* selB = selA + a.p2max;                                                // [p2max]
-  uint32_t* bstart = reinterpret_cast<uint32_t*>(selB);                      // [2048], over selB
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);           // [kHistSlots]
   int* wsum = reinterpret_cast<int*>(hist + kHistSlots);                     // [32]
   int* misc = wsum + 32;                                                     // [8]
@@ -354,7 +389,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   const int tid = threadIdx.x;
   const int topk = a.topk;
   const int kp = a.kpool;
-  const int t = blockIdx.x;
+  int t = blockIdx.x;
+  if (a.cls_map && !class_row(a, blockIdx.x, t)) return;
   const RowInfo cur = row_info(a, t);
   const int cand = cur.cand, nsel = cur.nsel;
   const int lo = cur.lo, u = cur.u, b = cur.b;
@@ -450,7 +486,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         for (int j = 0; j < 4; ++j) atomicAdd(&hist[bin[4 * e + j]], 1u);
       }
     __syncthreads();
-    scan_pass1_bins<NT>(hist, nsel, wsum, misc, bstart, kBucketMax);
+    scan_pass1_bins<NT>(hist, nsel, wsum, misc, kBucketMax);
     d1 = misc[0];
     a1 = misc[1];
     const int c1 = misc[2];
@@ -510,8 +546,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   }
 
   if (fast) {
-    // ---- selection straight into bin order: bins hold their candidates from bstart[d]
-    //      (the count in bins above d) on. Keys above thr are all taken; of the keys equal to
+    // ---- selection straight into bin order: bin d holds its candidates from slot
+    //      above(d) (the count in bins above it, the high half of its histogram word) on. Keys above thr are all taken; of the keys equal to
     //      thr (all in bin d1) the krem lowest indices, which needs their index order only
     //      when fewer are taken than exist.
     uint32_t eqtake = 0xFFFFFFFFu;   // bit 4e+j: a key equal to thr that is taken
@@ -552,7 +588,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     auto put = [&](int e, int j) {
       const uint32_t k = key[4 * e + j];
       const uint32_t d = (uint32_t)bin[4 * e + j];
-      const uint32_t slot = atomicAdd(&bstart[d], 1u);
+      const uint32_t slot = atomicAdd(&hist[d], 0x10000u) >> 16;
       ord[slot] = ((u64)(~k) << 32) | (d << 16) | (uint32_t)idx(e, j);
     };
     if (neq > krem) {
@@ -576,29 +612,49 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
     __syncthreads();
     // ---- each entry's rank inside its bin gives its output position. After the scatter
-    //      bstart[d] is the end of bin d; bins above d1 are taken whole, bin d1 from a1 on.
+    //      the high half of bin d's word is the end of its range; bins above d1 are taken
+    //      whole, bin d1 from a1 on. Two entries per thread at a time, so that their LDS
+    //      reads overlap; outputs go through buffer stores (32-bit offsets).
     float* os = a.out_scores + (long long)t * topk;
     const int width = kp == 1 ? topk : topk * kp + kp - 1;
     int32_t* oi = a.out_indices + (long long)t * width;
     int32_t* op = (kp > 1 && a.out_pool_indices) ? a.out_pool_indices + (long long)t * topk : nullptr;
     const int pbase = kp > 1 ? a.cu_pools[b] : 0;
-    for (int i = tid; i < nsel; i += NT) {
-      const u64 v = ord[i];
-      const uint32_t lw = (uint32_t)v;
-      const int d = (int)((lw >> 16) & 2047u);
-      const int end = (int)bstart[d];
-      const int s0 = d == d1 ? a1 : end - (int)hist[d];
-      int r = 0;
-      for (int q = s0; q < end; ++q) r += ord[q] < v;
-      const int dest = s0 + r;
-      const int ix = (int)(lw & 0xFFFFu);
-      os[dest] = key_score(~(uint32_t)(v >> 32));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(os, topk * 4);
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(oi, width * 4);
+    // Rank inside the bin of v among ord[s0, end): entries are read four at a time (reads
+    // past `end` stay inside the workgroup's LDS and are masked out).
+    auto store = [&](u64 v, int dest) {
+      const int ix = (int)((uint32_t)v & 0xFFFFu);
+      __builtin_amdgcn_raw_buffer_store_b32(f2u(key_score(~(uint32_t)(v >> 32))), rs, dest * 4, 0, 0);
       if (kp == 1) {
-        oi[dest] = lo + ix;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(lo + ix), ri, dest * 4, 0, 0);
       } else {
         if (op) op[dest] = pbase + ix;
-        for (int j = 0; j < kp; ++j) oi[dest * kp + j] = lo + ix * kp + j;
+        for (int j = 0; j < kp; ++j)
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(lo + ix * kp + j), ri, (dest * kp + j) * 4, 0, 0);
       }
+    };
+    for (int i0 = tid; i0 < nsel; i0 += 2 * NT) {
+      const bool two = i0 + NT < nsel;
+      const u64 v0 = ord[i0];
+      const u64 v1 = two ? ord[i0 + NT] : 0ull;
+      const int e0 = (int)(((uint32_t)v0 >> 16) & 2047u), e1 = (int)(((uint32_t)v1 >> 16) & 2047u);
+      const uint32_t w0 = hist[e0], w1 = hist[e1];
+      const int end0 = (int)(w0 >> 16), end1 = two ? (int)(w1 >> 16) : 0;
+      const int b0 = e0 == d1 ? a1 : end0 - (int)(w0 & 0xFFFFu);
+      const int b1 = two ? (e1 == d1 ? a1 : end1 - (int)(w1 & 0xFFFFu)) : 0;
+      int r0 = 0, r1 = 0;
+      for (int q = 0; b0 + q < end0 || b1 + q < end1; q += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u64 x0 = ord[b0 + q + j], x1 = ord[b1 + q + j];
+          r0 += b0 + q + j < end0 && x0 < v0;
+          r1 += b1 + q + j < end1 && x1 < v1;
+        }
+      }
+      store(v0, b0 + r0);
+      if (two) store(v1, b1 + r1);
     }
     for (int j = nsel + tid; j < topk; j += NT) os[j] = -INFINITY;
     if (kp == 1) {
@@ -647,7 +703,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     thr = prefix;
   }
 
-  // ---- compaction into selB[0, nsel): keys above thr (in any order: the ordering pass
+  // ---- compaction into selA[0, nsel): keys above thr (in any order: the ordering pass
   //      sorts them), then the krem lowest-index keys equal to thr. One block prefix sum of
   //      (above << 16 | equal) counts gives every thread its slots; only when fewer equal
   //      keys are taken than exist is their index order needed, from a second prefix sum
@@ -676,8 +732,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         for (int j = 0; j < 4; ++j) {
           const uint32_t k = key[4 * e + j];
           const u64 v = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
-          if (k > thr) selB[pos_gt++] = v;
-          else if (k == thr && k != 0u) selB[pos_eq++] = v;
+          if (k > thr) selA[pos_gt++] = v;
+          else if (k == thr && k != 0u) selA[pos_eq++] = v;
         }
       }
   } else {
@@ -709,7 +765,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
           for (int j = 0; j < 4; ++j) {
             const uint32_t k = key[4 * e + j];
             if (k == thr && k != 0u) {
-              if (rank < krem) selB[ngt + rank] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+              if (rank < krem) selA[ngt + rank] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
               ++rank;
             }
           }
@@ -723,20 +779,20 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t k = key[4 * e + j];
-          if (k > thr) selB[pos_gt++] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+          if (k > thr) selA[pos_gt++] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
         }
       }
   }
 
-  // ---- ordering of selB[0, nsel) by the bitonic network: rows that come here have scores
+  // ---- ordering of selA[0, nsel) by the bitonic network: rows that come here have scores
   //      that the linear bins do not separate (ties, clusters, no finite range)
   int n2 = 64;
   while (n2 < nsel) n2 <<= 1;
-  for (int i = nsel + tid; i < n2; i += NT) selB[i] = ~0ull;
+  for (int i = nsel + tid; i < n2; i += NT) selA[i] = ~0ull;
   __syncthreads();
-  if (n2 <= 128) bitonic_sort<1, NT>(selB, n2);
-  else bitonic_sort<4, NT>(selB, n2);
-  const u64* sel = selB;
+  if (n2 <= 128) bitonic_sort<1, NT>(selA, n2);
+  else bitonic_sort<4, NT>(selA, n2);
+  const u64* sel = selA;
 
   // ---- outputs
   float* os = a.out_scores + (long long)t * topk;
@@ -768,7 +824,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 }
 
 template <int NT, int EPT>
-hipError_t launch_cfg(const TopkArgs& a, size_t lds, hipStream_t st) {
+hipError_t launch_cfg(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
   // The dynamic LDS limit is raised only when a launch needs more than the default 64 KB,
   // and only to what it needs: the raised limit is what each workgroup reserves, so a
   // blanket 160 KB would leave one workgroup per CU. Done once per (device, size) and
@@ -786,7 +842,7 @@ hipError_t launch_cfg(const TopkArgs& a, size_t lds, hipStream_t st) {
       if (device < 64) set_to[device] = lds;
     }
   }
-  hipLaunchKernelGGL((topk_kernel<NT, EPT>), dim3(a.T), dim3(NT), lds, st, a);
+  hipLaunchKernelGGL((topk_kernel<NT, EPT>), dim3(grid), dim3(NT), lds, st, a);
   return hipGetLastError();
 }
 
@@ -798,12 +854,8 @@ int p2_of(int topk, int max_cand) {
 
 }  // namespace
 
-// Dynamic LDS layout: selA [p2max] u64 | selB [p2max] u64 in a region of at least 2048 u32
-// (the pass-1 bin starts overlay it) | hist [kHistSlots] u32 | wsum [32] | misc [8].
-int topk_hist_offset(int max_cand, int topk) {
-  const int p2 = p2_of(topk, max_cand);
-  return p2 * 8 + std::max(p2 * 8, 2048 * 4);
-}
+// Dynamic LDS layout: selA [p2max] u64 | hist [kHistSlots] u32 | wsum [32] | misc [8].
+int topk_hist_offset(int max_cand, int topk) { return p2_of(topk, max_cand) * 8; }
 
 size_t topk_lds_bytes(int max_cand, int topk) {
   return (size_t)topk_hist_offset(max_cand, topk) + kHistSlots * 4 + 32 * 4 + 8 * 4;
@@ -815,19 +867,46 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
   a.scores = p.scores; a.stride = p.stride; a.max_cand = p.max_cand;
   a.T = p.T; a.B = p.B; a.max_seqlen = p.max_seqlen; a.kpool = p.kpool; a.kpool_tail = p.kpool_tail;
   a.topk = p.topk;
-  a.p2max = p2_of(p.topk, p.max_cand);
-  a.hist_off = topk_hist_offset(p.max_cand, p.topk);
   a.cu = p.cu; a.cu_pools = p.cu_pools;
   a.out_indices = p.out_indices; a.out_scores = p.out_scores; a.out_lengths = p.out_lengths;
   a.out_pool_indices = p.out_pool_indices;
+  // Rows longer than 4096 candidates go to the smallest launch shape that holds them, one
+  // launch per size class, longest rows first: a document's early positions have few
+  // candidates and would otherwise run in the shape its longest row needs (fewer rows in
+  // flight, more waiting waves per row). Shorter rows share one launch: below 4096 the
+  // shapes differ little and an extra launch costs more than it saves.
   const int mc = p.max_cand;
-  const size_t lds = topk_lds_bytes(p.max_cand, p.topk);
-  if (mc <= 1024) return launch_cfg<256, 4>(a, lds, st);   // chunks of 4: at least 4 per thread
-  if (mc <= 2048) return launch_cfg<256, 8>(a, lds, st);
-  if (mc <= 4096) return launch_cfg<256, 16>(a, lds, st);
-  if (mc <= 8192) return launch_cfg<512, 16>(a, lds, st);
-  if (mc <= 16384) return launch_cfg<1024, 16>(a, lds, st);
-  return launch_cfg<1024, 32>(a, lds, st);
+  static const int kClassMax[] = {4096, 8192, 16384, kTopkMaxCand};
+  int nclass = 0;
+  while (kClassMax[nclass] < mc) ++nclass;
+  for (int c = nclass; c >= 0; --c) {
+    const int lo = c == 0 ? 0 : kClassMax[c - 1] + 1;
+    const int hi = std::min(kClassMax[c], mc);
+    a.cls_lo = lo; a.cls_hi = hi; a.cls_map = nclass > 0;
+    a.p2max = p2_of(p.topk, hi);
+    a.hist_off = topk_hist_offset(hi, p.topk);
+    const size_t lds = topk_lds_bytes(hi, p.topk);
+    long long grid = p.T;
+    if (c < nclass) {   // positions [lo*kp - 1, hi*kp + kp - 2] of each document
+      const long long ulo = lo == 0 ? 0 : (long long)lo * p.kpool - 1;
+      const long long uhi = (long long)hi * p.kpool + p.kpool - 2;
+      grid = std::min(grid, (long long)p.B * (uhi - ulo + 1));
+    }
+    if (grid <= 0) continue;
+    hipError_t e;
+    if (hi <= 1024) e = launch_cfg<256, 4>(a, lds, (int)grid, st);   // chunks of 4: at least 4 per thread
+    else if (hi <= 2048) e = launch_cfg<256, 8>(a, lds, (int)grid, st);
+    else if (hi <= 4096) e = launch_cfg<256, 16>(a, lds, (int)grid, st);
+    // Longer rows take more candidates per thread rather than wider workgroups: a
+    // workgroup's serial steps (block reductions, the one-wave threshold ranking) then cost
+    // fewer waiting waves, and more rows are in flight per CU (measured: 8193-candidate rows
+    // 1.5x faster as 256 x 32 than as 1024 x 16).
+    else if (hi <= 8192) e = launch_cfg<256, 32>(a, lds, (int)grid, st);
+    else if (hi <= 16384) e = launch_cfg<512, 32>(a, lds, (int)grid, st);
+    else e = launch_cfg<1024, 32>(a, lds, (int)grid, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace dsa

@@ -8,7 +8,8 @@ ordering), ties at the threshold with fewer taken than exist, a bin above the th
 holding more than its ordering limit, a clustered threshold bin (radix select), an outlier
 that crushes the linear bins, constant rows, small integers (ties everywhere), signed
 zeros, negative rows and magnitudes from subnormal to 1e30. Document lengths select each
-of the launch shapes (up to 1024, 2048, 4096, 8192, 16384 and 32768 candidates per row).
+of the launch shapes (up to 1024, 2048, 4096, 8192, 16384 and 32768 candidates per row), and
+rows of one call fall in several launch size classes, over more than 64 documents.
 """
 
 import numpy as np
@@ -57,40 +58,61 @@ def _row(p, cand, topk, rng):
     return v
 
 
-def _sample_rows(L, topk, rng):
-    rows = set(range(max(0, L - 12), L))
-    rows |= {t for t in (0, 1, 2, 63, 64, 65, topk - 2, topk - 1, topk, topk + 1) if 0 <= t < L}
-    rows |= set(int(x) for x in rng.choice(L, size=min(L, 40), replace=False))
+def _sample_rows(docs, topk, rng):
+    cu = np.concatenate([[0], np.cumsum(docs)])
+    rows = set()
+    for b, n in enumerate(docs):
+        lo = int(cu[b])
+        rows |= {lo + u for u in range(max(0, n - 6), n)}
+        rows |= {lo + u for u in (0, 1, 63, 64, topk - 1, topk, 4095, 4096, 8191, 8192) if 0 <= u < n}
+    T = int(cu[-1])
+    rows |= set(int(x) for x in rng.choice(T, size=min(T, 40), replace=False))
     return sorted(rows)
 
 
-def _run(L, topk, kp, tail, seed):
+def _run(docs, topk, kp, tail, seed):
     import torch
     import sparse_attention_indexer_dsa_amd as dsa
     rng = np.random.default_rng(seed)
+    docs = [int(n) for n in docs]
+    cu_h = np.concatenate([[0], np.cumsum(docs)]).astype(np.int64)
+    T, L = int(cu_h[-1]), max(docs)
+    doc_of = np.repeat(np.arange(len(docs)), docs)
+    pos = np.arange(T) - cu_h[doc_of]
     max_cand = L if kp == 1 else L // kp
     stride = (max(1, max_cand) + 63) // 64 * 64
     gen_t = torch.Generator(device="cuda").manual_seed(seed)
-    flat = torch.randn(L * stride + 64, generator=gen_t, device="cuda", dtype=torch.float32) * 3.0
-    ws = flat[:L * stride].view(L, stride)     # the library asks for 256 bytes beyond the rows
-    rows = _sample_rows(L, topk, rng)
+    flat = torch.randn(T * stride + 64, generator=gen_t, device="cuda", dtype=torch.float32) * 3.0
+    ws = flat[:T * stride].view(T, stride)     # the library asks for 256 bytes beyond the rows
+    rows = _sample_rows(docs, topk, rng)
     want = {}
     for i, t in enumerate(rows):
-        cand = (t + 1) // kp
+        cand = (int(pos[t]) + 1) // kp
         if cand == 0:
             continue
         v = _row(i % NPAT, cand, topk, rng)
         ws[t, :cand] = torch.from_numpy(v).cuda()
         want[t] = v
-    # rows left random are checked too: read back after the call
-    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
-    cu_pools = torch.tensor([0, L // kp], dtype=torch.int32, device="cuda") if kp > 1 else None
-    out = dsa.topk(flat, L, cu, L, topk, kpool=kp, cu_pools=cu_pools, kpool_tail=tail)
+    cu = torch.tensor(cu_h, dtype=torch.int32, device="cuda")
+    cu_pools = (torch.tensor(np.concatenate([[0], np.cumsum([n // kp for n in docs])]), dtype=torch.int32,
+                             device="cuda") if kp > 1 else None)
+    out = dsa.topk(flat, T, cu, L, topk, kpool=kp, cu_pools=cu_pools, kpool_tail=tail)
     torch.cuda.synchronize()
-    extra = [int(x) for x in rng.choice(L, size=min(L, 16), replace=False)]
     host = {n: out[n].cpu().numpy() for n in out}
+    # every row was handled: its length is fixed by its position alone
+    cand_all = (pos + 1) // kp
+    nsel_all = np.minimum(topk, cand_all)
+    if kp == 1:
+        assert np.array_equal(host["lengths"], nsel_all)
+    else:
+        tails = ((pos + 1) % kp) if tail else 0
+        assert np.array_equal(host["lengths"], nsel_all * kp + tails)
+    # rows left random are checked too: read back after the call
+    extra = [int(x) for x in rng.choice(T, size=min(T, 16), replace=False)]
+    pbase = np.concatenate([[0], np.cumsum([n // kp for n in docs])])
     for t in sorted(set(want) | set(extra)):
-        cand = (t + 1) // kp
+        b, u = int(doc_of[t]), int(pos[t])
+        cand = (u + 1) // kp
         v = want[t] if t in want else ws[t, :cand].cpu().numpy()
         sel, s = orc.topk_row(v.astype(np.float64), topk)
         n = sel.size
@@ -99,16 +121,14 @@ def _run(L, topk, kp, tail, seed):
         assert np.all(np.isneginf(sc[n:])), t
         if kp == 1:
             idx = host["indices"][t].astype(np.int64)
-            assert host["lengths"][t] == n, (t, host["lengths"][t], n)
-            assert np.array_equal(idx[:n], sel), (t, idx[:8], sel[:8])
+            assert np.array_equal(idx[:n] - cu_h[b], sel), (t, idx[:8], sel[:8])
             assert np.all(idx[n:] == -1), t
         else:
             pidx = host["pool_indices"][t].astype(np.int64)
-            assert np.array_equal(pidx[:n], sel), (t, pidx[:8], sel[:8])
+            assert np.array_equal(pidx[:n] - pbase[b], sel), (t, pidx[:8], sel[:8])
             assert np.all(pidx[n:] == -1), t
-            toks = orc.expand(sel, t, kp, 0, tail)
+            toks = orc.expand(sel, u, kp, int(cu_h[b]), tail)
             tok = host["indices"][t].astype(np.int64)
-            assert host["lengths"][t] == toks.size, t
             assert np.array_equal(tok[:toks.size], toks), t
             assert np.all(tok[toks.size:] == -1), t
 
@@ -116,9 +136,20 @@ def _run(L, topk, kp, tail, seed):
 @pytest.mark.parametrize("L, topk", [(1000, 64), (2000, 256), (3000, 7), (4000, 512), (8000, 2048),
                                      (16000, 2048), (32768, 2048), (1500, 2048)])
 def test_selection_patterns(L, topk):
-    _run(L, topk, 1, True, L + topk)
+    _run([L], topk, 1, True, L + topk)
 
 
 @pytest.mark.parametrize("tail", [True, False])
 def test_selection_patterns_kpool(tail):
-    _run(8000, 512, 4, tail, 11 + tail)
+    _run([8000], 512, 4, tail, 11 + tail)
+
+
+@pytest.mark.parametrize("kp", [1, 4])
+def test_selection_many_documents(kp):
+    # more than 64 documents (the row map takes them 64 at a time), empty ones, and long
+    # ones whose rows fall in several launch size classes
+    rng = np.random.default_rng(70 + kp)
+    docs = rng.integers(0, 1500, 70)
+    docs[[3, 17, 40]] = 0
+    docs[[5, 66]] = [9000, 5000] if kp == 1 else [20000, 36000]
+    _run(docs, 256, kp, True, 80 + kp)
