@@ -329,6 +329,7 @@ __device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* w
 constexpr int kValueList = 64;   // a threshold bin this small is resolved by counting
 constexpr int kBucketMax = 64;   // a selected pass-1 bin larger than this: bitonic ordering instead
 constexpr int kHistSlots = 2048 + 16;   // pass-1 bins, then a slot that counts non-candidates
+constexpr int kFallbackGrid = 256;      // workgroups of the fallback launch
 
 struct RowInfo {
   int t, b, lo, u, cand, nsel;
@@ -344,6 +345,54 @@ __device__ __forceinline__ RowInfo row_info(const TopkArgs& a, int t) {
   r.nsel = min(a.topk, r.cand);
   return r;
 }
+
+// Output rows of query t: entries in selection order at positions dest < nsel (score bits and
+// the candidate's document-local index), then padding (-inf / -1, KPool tail tokens) and the
+// length. Buffer stores take 32-bit offsets.
+struct RowOut {
+  float* os; int32_t* oi; int32_t* op;
+  __amdgpu_buffer_rsrc_t rs, ri;
+  int topk, kp, width, lo, pbase;
+  __device__ __forceinline__ RowOut(const TopkArgs& a, int t, int lo_, int b) {
+    topk = a.topk; kp = a.kpool; lo = lo_;
+    width = kp == 1 ? topk : topk * kp + kp - 1;
+    os = a.out_scores + (long long)t * topk;
+    oi = a.out_indices + (long long)t * width;
+    op = (kp > 1 && a.out_pool_indices) ? a.out_pool_indices + (long long)t * topk : nullptr;
+    pbase = kp > 1 ? a.cu_pools[b] : 0;
+    rs = make_rsrc(os, topk * 4);
+    ri = make_rsrc(oi, width * 4);
+  }
+  __device__ __forceinline__ void store(int dest, uint32_t score_bits, int ix) const {
+    __builtin_amdgcn_raw_buffer_store_b32(score_bits, rs, dest * 4, 0, 0);
+    if (kp == 1) {
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(lo + ix), ri, dest * 4, 0, 0);
+    } else {
+      if (op) op[dest] = pbase + ix;
+      for (int j = 0; j < kp; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(lo + ix * kp + j), ri, (dest * kp + j) * 4, 0, 0);
+    }
+  }
+  // padding after the first nsel entries, the KPool tail, the length (thread 0)
+  template <int NT>
+  __device__ __forceinline__ void finish(const TopkArgs& a, int t, int nsel, int u) const {
+    const int tid = threadIdx.x;
+    for (int j = nsel + tid; j < topk; j += NT) os[j] = -INFINITY;
+    if (kp == 1) {
+      for (int j = nsel + tid; j < topk; j += NT) oi[j] = -1;
+      if (tid == 0) a.out_lengths[t] = nsel;
+    } else {
+      if (op)
+        for (int j = nsel + tid; j < topk; j += NT) op[j] = -1;
+      const int tail = a.kpool_tail ? (u + 1) % kp : 0;
+      const int npool_tok = nsel * kp;
+      const int tail_start = lo + (u / kp) * kp;
+      for (int s2 = npool_tok + tid; s2 < width; s2 += NT)
+        oi[s2] = s2 < npool_tok + tail ? tail_start + (s2 - npool_tok) : -1;
+      if (tid == 0) a.out_lengths[t] = npool_tok + tail;
+    }
+  }
+};
 
 // Row of block j among the rows whose candidate count lies in [cls_lo, cls_hi] (documents in
 // order, positions ascending); false when j is past them. Candidate counts grow with the
@@ -391,24 +440,38 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   const int kp = a.kpool;
   int t = blockIdx.x;
   if (a.cls_map && !class_row(a, blockIdx.x, t)) return;
+  t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the row's values in scalar registers
   const RowInfo cur = row_info(a, t);
   const int cand = cur.cand, nsel = cur.nsel;
   const int lo = cur.lo, u = cur.u, b = cur.b;
 
-  // ---- the row's scores as order-preserving keys (0: no candidate). Thread tid holds the
-  //      4-candidate chunks c = e*NT + tid (candidates 4c .. 4c+3), so one load instruction
-  //      covers 16*NT consecutive bytes, and a chunk group e lies entirely past the row once
-  //      4*e*NT >= cand: such groups are skipped by every per-candidate pass (uniform branch).
-  //      All loads are issued before any is used; the buffer descriptor ends at the row's
-  //      last candidate, so loads of groups past it return zeros without touching memory.
+  // ---- the row's scores in registers. Thread tid holds the 4-candidate chunks
+  //      c = e*NT + tid (candidates 4c .. 4c+3), so one load instruction covers 16*NT
+  //      consecutive bytes, and a chunk group e lies entirely past the row once 4*e*NT >= cand:
+  //      such groups are skipped by every per-candidate pass (uniform branch). Only the last
+  //      live group can hold slots past the row (`in` below). All loads are issued before any
+  //      is used; the buffer descriptor ends at the row's last candidate, so loads of groups
+  //      past it return zeros without touching memory. Up to 16 candidates per thread the
+  //      order-preserving keys (0 past the row) and the pass-1 bins are kept in registers;
+  //      with 32 only the scores are (-0 folded onto +0) and keys and bins are recomputed
+  //      where needed: a few more instructions, but 64 fewer registers, which keeps 8 waves
+  //      per SIMD (more rows in flight).
   static_assert(EPT % 4 == 0, "candidates are held in chunks of 4");
   static_assert(EPT <= 32, "one bit per candidate in a 32-bit mask");
   constexpr int NCH = EPT / 4;
   auto live = [&](int e) { return 4 * e * NT < cand; };
   auto full = [&](int e) { return 4 * (e + 1) * NT <= cand; };
   auto idx = [&](int e, int j) { return 4 * (e * NT + tid) + j; };
-  uint32_t key[EPT];                       // defined for the chunk groups that are live
-  float val[EPT];                          // the scores themselves (finite; -0 folded to +0)
+  auto in = [&](int e, int j) { return full(e) || idx(e, j) < cand; };
+  // order-preserving key of a score: negative scores invert all bits, others set the sign bit
+  auto keyof = [](float x) {
+    const uint32_t v = f2u(x);
+    return v ^ ((uint32_t)((int)v >> 31) | 0x80000000u);
+  };
+  constexpr bool KEEP = EPT <= 16;
+  float val[EPT];
+  uint32_t keyA[KEEP ? EPT : 1];
+  int binA[KEEP ? EPT : 1];
   uint32_t kmax = 0, kmin = 0xFFFFFFFFu;   // over candidates only
   {
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.scores + (long long)t * a.stride, cand * 4);
@@ -420,25 +483,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       if (!live(e)) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
-        const uint32_t uu = f2u(x);
-        // order-preserving key: negative scores invert all bits, others set the sign bit
-        key[4 * e + j] = uu ^ ((uint32_t)((int)uu >> 31) | 0x80000000u);
-        val[4 * e + j] = x;
-      }
-      if (full(e)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kmax = max(kmax, key[4 * e + j]);
-          kmin = min(kmin, key[4 * e + j]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool in = idx(e, j) < cand;
-          key[4 * e + j] = in ? key[4 * e + j] : 0u;
-          kmax = max(kmax, key[4 * e + j]);
-          kmin = in ? min(kmin, key[4 * e + j]) : kmin;
+        val[4 * e + j] = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
+        const uint32_t k = keyof(val[4 * e + j]);
+        if (full(e)) {
+          kmax = max(kmax, k);
+          kmin = min(kmin, k);
+          if constexpr (KEEP) keyA[4 * e + j] = k;
+        } else if (idx(e, j) < cand) {
+          kmax = max(kmax, k);
+          kmin = min(kmin, k);
+          if constexpr (KEEP) keyA[4 * e + j] = k;
+        } else {
+          if constexpr (KEEP) keyA[4 * e + j] = 0u;
         }
       }
     }
@@ -446,6 +502,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 
   // ---- key range of the row's candidates (max and min in one reduction)
   block_minmax<NT>(kmin, kmax, wsum);
+  const RowOut out(a, t, lo, b);
+  if (cand == 0 || kmin == kmax) {
+    // no candidate, or all scores equal: the lowest indices, in index order
+    for (int j = tid; j < nsel; j += NT) out.store(j, f2u(key_score(kmin)), j);
+    out.finish<NT>(a, t, nsel, u);
+    return;
+  }
 
   uint32_t thr = kmin;   // every selected key is >= thr
   int krem = cand;       // candidates equal to thr that are taken (lowest indices first)
@@ -455,27 +518,30 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   int d1 = 0, a1 = 0;    // the threshold bin and the count of candidates in bins above it
   const float vmin = key_score(kmin), vmax = key_score(kmax);
   const float span = vmax - vmin;
-  int bin[EPT];
-  if (span > 0.f && span < INFINITY) {
+  const bool finite = span > 0.f && span < INFINITY;   // every candidate score finite, not all equal
+  const float vscale = finite ? 2048.f / span : 0.f;
+  const float voff = -vmin * vscale;
+  // pass-1 bin: (v - vmin) * 2048 / span as one fma (any rounding keeps the bins monotone in v)
+  auto binof = [&](float x) { return min(2047, max(0, (int)__builtin_fmaf(x, vscale, voff))); };
+  // Accessors over the two register layouts. With KEEP, slots past the row carry key 0 and a
+  // bin of 2048 or more, so no comparison below selects them without the `in` test.
+  auto keyat = [&](int e, int j) {
+    if constexpr (KEEP) return keyA[4 * e + j]; else return keyof(val[4 * e + j]);
+  };
+  auto binat = [&](int e, int j) {
+    if constexpr (KEEP) return binA[4 * e + j]; else return binof(val[4 * e + j]);
+  };
+  auto cand_at = [&](int e, int j) {
+    if constexpr (KEEP) return true; else return in(e, j);
+  };
+  if (finite) {
     // ---- pass 1: 2048 bins linear in the score over [vmin, vmax]. Bins are monotone in the
     //      score, and a smooth score distribution spreads evenly over them, so the LDS
     //      atomics rarely collide and the threshold bin holds few candidates. The same bins
     //      then order the selection: bins at and above the threshold bin, taken from the
     //      top, are the selection in descending order up to the order inside each bin.
-    const float vscale = 2048.f / span;
-    const float voff = -vmin * vscale;
-    // bin = (v - vmin) * 2048 / span as one fma (any rounding keeps the bins monotone in v);
-    // non-candidates of the row's last chunk group count in slots 2048..2063 (spread over
-    // banks so that their atomics do not serialise on one address)
-#pragma unroll
-    for (int e = 0; e < NCH; ++e)
-      if (live(e)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int bb = min(2047, max(0, (int)__builtin_fmaf(val[4 * e + j], vscale, voff)));
-          bin[4 * e + j] = full(e) || key[4 * e + j] != 0u ? bb : 2048 + (tid & 15);
-        }
-      }
+    //      Slots past the row count in 2048..2063 (spread over banks so that their atomics
+    //      do not serialise on one address).
     for (int i = tid; i < kHistSlots / 4; i += NT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) { misc[5] = 0; misc[6] = 0; }
     __syncthreads();
@@ -483,7 +549,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     for (int e = 0; e < NCH; ++e)
       if (live(e)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&hist[bin[4 * e + j]], 1u);
+        for (int j = 0; j < 4; ++j) {
+          const int d = in(e, j) ? binof(val[4 * e + j]) : 2048 + (tid & 15);
+          if constexpr (KEEP) binA[4 * e + j] = d;
+          atomicAdd(&hist[d], 1u);
+        }
       }
     __syncthreads();
     scan_pass1_bins<NT>(hist, nsel, wsum, misc, kBucketMax);
@@ -497,25 +567,30 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       // the krem1-th largest among them by counting over lane values
       uint32_t* list = reinterpret_cast<uint32_t*>(selA);
       {
+        uint32_t hit = 0;   // bit 4e+j: candidate in bin d1
         int mine = 0;
 #pragma unroll
         for (int e = 0; e < NCH; ++e)
           if (live(e)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mine += bin[4 * e + j] == d1;
+            for (int j = 0; j < 4; ++j) {
+              const bool h = cand_at(e, j) && binat(e, j) == d1;
+              hit |= (uint32_t)h << (4 * e + j);
+              mine += h;
+            }
           }
         const int incl = wave_prefix_sum(mine);
         const int wtot = __builtin_amdgcn_readlane(incl, 63);
         int base = 0;
         if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&misc[5], wtot);
         int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
-        if (mine > 0) {
+        if (hit) {
 #pragma unroll
           for (int e = 0; e < NCH; ++e)
             if (live(e)) {
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (bin[4 * e + j] == d1) list[pos++] = key[4 * e + j];
+                if ((hit >> (4 * e + j)) & 1u) list[pos++] = keyat(e, j);
             }
         }
       }
@@ -547,10 +622,22 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 
   if (fast) {
     // ---- selection straight into bin order: bin d holds its candidates from slot
-    //      above(d) (the count in bins above it, the high half of its histogram word) on. Keys above thr are all taken; of the keys equal to
-    //      thr (all in bin d1) the krem lowest indices, which needs their index order only
-    //      when fewer are taken than exist.
-    uint32_t eqtake = 0xFFFFFFFFu;   // bit 4e+j: a key equal to thr that is taken
+    //      above(d) (the count in bins above it, the high half of its histogram word) on.
+    //      Scores above the threshold score are all taken; of those equal to it (all in bin
+    //      d1) the krem lowest indices, which needs their index order only when fewer are
+    //      taken than exist. Every score here is finite, so float comparisons order exactly
+    //      as the keys do.
+    const float vthr = key_score(thr);
+    auto is_eq = [&](int e, int j) {
+      if constexpr (KEEP) return keyA[4 * e + j] == thr; else return in(e, j) && val[4 * e + j] == vthr;
+    };
+    auto is_gt = [&](int e, int j) {
+      if constexpr (KEEP) return keyA[4 * e + j] > thr; else return in(e, j) && val[4 * e + j] > vthr;
+    };
+    auto is_ge = [&](int e, int j) {
+      if constexpr (KEEP) return keyA[4 * e + j] >= thr; else return in(e, j) && val[4 * e + j] >= vthr;
+    };
+    uint32_t eqtake = 0xFFFFFFFFu;   // bit 4e+j: a score equal to the threshold that is taken
     if (neq > krem) {
       // group e's equal keys come after all equal keys of groups < e; inside group e, thread
       // order then position in the chunk. Fields of 16 bits, two groups per prefix sum.
@@ -561,8 +648,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         int c0 = 0, c1 = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (live(e2)) c0 += key[4 * e2 + j] == thr;
-          if (e2 + 1 < NCH && live(e2 + 1)) c1 += key[4 * (e2 + 1) + j] == thr;
+          if (live(e2)) c0 += is_eq(e2, j);
+          if (e2 + 1 < NCH && live(e2 + 1)) c1 += is_eq(e2 + 1, j);
         }
         int gtot;
         const int gb = block_exclusive_sum<NT>((c1 << 16) | c0, wsum, gtot);
@@ -573,7 +660,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             int rank = eq_before_group + (h ? gb >> 16 : gb & 0xFFFF);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (key[4 * e + j] == thr) {
+              if (is_eq(e, j)) {
                 if (rank < krem) eqtake |= 1u << (4 * e + j);
                 ++rank;
               }
@@ -586,20 +673,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     // (score descending, index ascending); indices are < 2^16 and bins < 2^11.
     u64* ord = selA;
     auto put = [&](int e, int j) {
-      const uint32_t k = key[4 * e + j];
-      const uint32_t d = (uint32_t)bin[4 * e + j];
+      const uint32_t d = (uint32_t)binat(e, j);
       const uint32_t slot = atomicAdd(&hist[d], 0x10000u) >> 16;
-      ord[slot] = ((u64)(~k) << 32) | (d << 16) | (uint32_t)idx(e, j);
+      ord[slot] = ((u64)(~keyat(e, j)) << 32) | (d << 16) | (uint32_t)idx(e, j);
     };
     if (neq > krem) {
 #pragma unroll
       for (int e = 0; e < NCH; ++e)
         if (live(e)) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t k = key[4 * e + j];
-            if (k > thr || (k == thr && ((eqtake >> (4 * e + j)) & 1u))) put(e, j);
-          }
+          for (int j = 0; j < 4; ++j)
+            if (is_gt(e, j) || (is_eq(e, j) && ((eqtake >> (4 * e + j)) & 1u))) put(e, j);
         }
     } else {
 #pragma unroll
@@ -607,33 +691,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         if (live(e)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (key[4 * e + j] >= thr) put(e, j);
+            if (is_ge(e, j)) put(e, j);
         }
     }
     __syncthreads();
     // ---- each entry's rank inside its bin gives its output position. After the scatter
     //      the high half of bin d's word is the end of its range; bins above d1 are taken
     //      whole, bin d1 from a1 on. Two entries per thread at a time, so that their LDS
-    //      reads overlap; outputs go through buffer stores (32-bit offsets).
-    float* os = a.out_scores + (long long)t * topk;
-    const int width = kp == 1 ? topk : topk * kp + kp - 1;
-    int32_t* oi = a.out_indices + (long long)t * width;
-    int32_t* op = (kp > 1 && a.out_pool_indices) ? a.out_pool_indices + (long long)t * topk : nullptr;
-    const int pbase = kp > 1 ? a.cu_pools[b] : 0;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(os, topk * 4);
-    const __amdgpu_buffer_rsrc_t ri = make_rsrc(oi, width * 4);
-    // Rank inside the bin of v among ord[s0, end): entries are read four at a time (reads
-    // past `end` stay inside the workgroup's LDS and are masked out).
+    //      reads overlap; a bin is read four entries at a time (reads past its end stay
+    //      inside the workgroup's LDS and are masked out).
     auto store = [&](u64 v, int dest) {
-      const int ix = (int)((uint32_t)v & 0xFFFFu);
-      __builtin_amdgcn_raw_buffer_store_b32(f2u(key_score(~(uint32_t)(v >> 32))), rs, dest * 4, 0, 0);
-      if (kp == 1) {
-        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(lo + ix), ri, dest * 4, 0, 0);
-      } else {
-        if (op) op[dest] = pbase + ix;
-        for (int j = 0; j < kp; ++j)
-          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(lo + ix * kp + j), ri, (dest * kp + j) * 4, 0, 0);
-      }
+      out.store(dest, f2u(key_score(~(uint32_t)(v >> 32))), (int)((uint32_t)v & 0xFFFFu));
     };
     for (int i0 = tid; i0 < nsel; i0 += 2 * NT) {
       const bool two = i0 + NT < nsel;
@@ -656,26 +724,37 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       store(v0, b0 + r0);
       if (two) store(v1, b1 + r1);
     }
-    for (int j = nsel + tid; j < topk; j += NT) os[j] = -INFINITY;
-    if (kp == 1) {
-      for (int j = nsel + tid; j < topk; j += NT) oi[j] = -1;
-      if (tid == 0) a.out_lengths[t] = nsel;
-    } else {
-      if (op)
-        for (int j = nsel + tid; j < topk; j += NT) op[j] = -1;
-      const int tail = a.kpool_tail ? (u + 1) % kp : 0;
-      const int npool_tok = nsel * kp;
-      const int tail_start = lo + (u / kp) * kp;
-      for (int s2 = npool_tok + tid; s2 < width; s2 += NT)
-        oi[s2] = s2 < npool_tok + tail ? tail_start + (s2 - npool_tok) : -1;
-      if (tid == 0) a.out_lengths[t] = npool_tok + tail;
-    }
+    out.finish<NT>(a, t, nsel, u);
     return;
   }
 
-  if (!resolved) {
-    // ---- clustered rows (or no usable score range): radix select on the key bits
-    //      (11 + 11 + 10)
+  // Rows the bins do not separate (a clustered threshold bin, a selected bin of more than
+  // kBucketMax keys, no finite score range) are left to topk_fallback_kernel, which finds
+  // them by this negative length. Finishing them here would double this kernel's registers
+  // (fewer rows in flight for every row) to save one launch.
+  if (tid == 0) a.out_lengths[t] = -1;
+}
+
+// One row the bin ordering does not handle (a clustered threshold bin, a selected bin of more
+// than kBucketMax keys, no finite score range), by the whole workgroup, from its keys in
+// registers (0: no candidate, candidate c in key[4e+j] with c = 4(e*NT + tid) + j): the
+// topk-th largest key by an 11 + 11 + 10-bit radix select; compaction by block prefix sums
+// (keys above the threshold in any order, then the krem lowest-index keys equal to it);
+// ordering by the bitonic network.
+template <int NT, int EPT>
+__device__ __forceinline__ void fallback_keys(const TopkArgs& a, const RowInfo& cur, const uint32_t (&key)[EPT],
+                                              u64* sel, uint32_t* hist, int* wsum, int* misc) {
+  static_assert(EPT % 4 == 0, "candidates are held in chunks of 4");
+  constexpr int NCH = EPT / 4;
+  const int tid = threadIdx.x;
+  const int topk = a.topk;
+  const int t = cur.t;
+  const int cand = cur.cand, nsel = cur.nsel;
+  auto live = [&](int e) { return 4 * e * NT < cand; };
+  auto idx = [&](int e, int j) { return 4 * (e * NT + tid) + j; };
+  uint32_t thr = 1u;    // every selected key is >= thr (all candidates when cand <= topk)
+  int krem = cand;      // keys equal to thr that are taken, lowest indices first
+  if (cand > topk) {
     uint32_t prefix = 0, pmask = 0;
     krem = topk;
 #pragma unroll 1
@@ -683,7 +762,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
       const int nbins = pass == 2 ? 1024 : 2048;
       __syncthreads();
-      for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+      for (int q = tid; q < 2048; q += NT) hist[q] = 0;
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < NCH; ++e)
@@ -703,11 +782,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     thr = prefix;
   }
 
-  // ---- compaction into selA[0, nsel): keys above thr (in any order: the ordering pass
-  //      sorts them), then the krem lowest-index keys equal to thr. One block prefix sum of
-  //      (above << 16 | equal) counts gives every thread its slots; only when fewer equal
-  //      keys are taken than exist is their index order needed, from a second prefix sum
-  //      with one count field per chunk group (index order is group-major).
+  // ---- compaction into sel[0, nsel): one block prefix sum of (above << 16 | equal)
+  //      counts gives every thread its slots; only when fewer equal keys are taken than
+  //      exist is their index order needed, from a second prefix sum with one count field
+  //      per chunk group (index order is group-major)
   int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int e = 0; e < NCH; ++e)
@@ -721,9 +799,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
   int tot;
   const int before = block_exclusive_sum<NT>((n_gt << 16) | n_eq, wsum, tot);
-  const int ngt = tot >> 16, neq_all = tot & 0xFFFF;
+  const int ngt = tot >> 16, neq = tot & 0xFFFF;
   int pos_gt = before >> 16;
-  if (neq_all <= krem) {
+  if (neq <= krem) {
     int pos_eq = ngt + (before & 0xFFFF);
 #pragma unroll
     for (int e = 0; e < NCH; ++e)
@@ -732,24 +810,22 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         for (int j = 0; j < 4; ++j) {
           const uint32_t k = key[4 * e + j];
           const u64 v = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
-          if (k > thr) selA[pos_gt++] = v;
-          else if (k == thr && k != 0u) selA[pos_eq++] = v;
+          if (k > thr) sel[pos_gt++] = v;
+          else if (k == thr && k != 0u) sel[pos_eq++] = v;
         }
       }
   } else {
-    // group e's equal keys come after all equal keys of groups < e; inside group e, thread
-    // order then position in the chunk. Fields of 16 bits, two groups per prefix sum.
+    // group e's equal keys come after all equal keys of groups < e; inside group e,
+    // thread order then position in the chunk. Fields of 16 bits, two groups per sum.
     int eq_before_group = 0;
 #pragma unroll
     for (int e2 = 0; e2 < NCH; e2 += 2) {
       int c0 = 0, c1 = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (live(e2)) {
-          const uint32_t k0 = key[4 * e2 + j];
-          c0 += k0 == thr && k0 != 0u;
-        }
-        if (e2 + 1 < NCH && live(e2 + 1)) {
+        const uint32_t k0 = key[4 * e2 + j];
+        c0 += k0 == thr && k0 != 0u;
+        if (e2 + 1 < NCH) {
           const uint32_t k1 = key[4 * (e2 + 1) + j];
           c1 += k1 == thr && k1 != 0u;
         }
@@ -759,13 +835,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int e = e2 + h;
-        if (e < NCH && live(e)) {
-          int rank = eq_before_group + ((h ? gb >> 16 : gb & 0xFFFF));
+        if (e < NCH) {
+          int rank = eq_before_group + (h ? gb >> 16 : gb & 0xFFFF);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t k = key[4 * e + j];
             if (k == thr && k != 0u) {
-              if (rank < krem) selA[ngt + rank] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+              if (rank < krem) sel[ngt + rank] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
               ++rank;
             }
           }
@@ -779,71 +855,106 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t k = key[4 * e + j];
-          if (k > thr) selA[pos_gt++] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
+          if (k > thr) sel[pos_gt++] = ((u64)(~k) << 32) | (uint32_t)idx(e, j);
         }
       }
   }
 
-  // ---- ordering of selA[0, nsel) by the bitonic network: rows that come here have scores
-  //      that the linear bins do not separate (ties, clusters, no finite range)
+  // ---- ordering by the bitonic network, then the outputs
   int n2 = 64;
   while (n2 < nsel) n2 <<= 1;
-  for (int i = nsel + tid; i < n2; i += NT) selA[i] = ~0ull;
+  for (int q = nsel + tid; q < n2; q += NT) sel[q] = ~0ull;
   __syncthreads();
-  if (n2 <= 128) bitonic_sort<1, NT>(selA, n2);
-  else bitonic_sort<4, NT>(selA, n2);
-  const u64* sel = selA;
-
-  // ---- outputs
-  float* os = a.out_scores + (long long)t * topk;
-  for (int j = tid; j < topk; j += NT)
-    os[j] = j < nsel ? key_score(~(uint32_t)(sel[j] >> 32)) : -INFINITY;
-  if (kp == 1) {
-    int32_t* oi = a.out_indices + (long long)t * topk;
-    for (int j = tid; j < topk; j += NT) oi[j] = j < nsel ? lo + (int)(uint32_t)sel[j] : -1;
-    if (tid == 0) a.out_lengths[t] = nsel;
-  } else {
-    const int pbase = a.cu_pools[b];
-    if (a.out_pool_indices) {
-      int32_t* op = a.out_pool_indices + (long long)t * topk;
-      for (int j = tid; j < topk; j += NT) op[j] = j < nsel ? pbase + (int)(uint32_t)sel[j] : -1;
-    }
-    const int tail = a.kpool_tail ? (u + 1) % kp : 0;
-    const int width = topk * kp + kp - 1;
-    const int npool_tok = nsel * kp;
-    const int tail_start = lo + (u / kp) * kp;
-    int32_t* oi = a.out_indices + (long long)t * width;
-    for (int s2 = tid; s2 < width; s2 += NT) {
-      int v = -1;
-      if (s2 < npool_tok) v = lo + (int)(uint32_t)sel[s2 / kp] * kp + s2 % kp;
-      else if (s2 < npool_tok + tail) v = tail_start + (s2 - npool_tok);
-      oi[s2] = v;
-    }
-    if (tid == 0) a.out_lengths[t] = npool_tok + tail;
-  }
+  if (n2 <= 128) bitonic_sort<1, NT>(sel, n2);
+  else bitonic_sort<4, NT>(sel, n2);
+  const RowOut out(a, t, cur.lo, cur.b);
+  for (int j = tid; j < nsel; j += NT)
+    out.store(j, f2u(key_score(~(uint32_t)(sel[j] >> 32))), (int)(uint32_t)sel[j]);
+  out.finish<NT>(a, t, nsel, cur.u);
+  __syncthreads();   // the row's LDS is reused by the next flagged row
 }
 
 template <int NT, int EPT>
-hipError_t launch_cfg(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
-  // The dynamic LDS limit is raised only when a launch needs more than the default 64 KB,
-  // and only to what it needs: the raised limit is what each workgroup reserves, so a
-  // blanket 160 KB would leave one workgroup per CU. Done once per (device, size) and
-  // never inside graph capture (it is not a stream operation).
+__device__ __forceinline__ void fallback_row(const TopkArgs& a, int t, u64* sel, uint32_t* hist, int* wsum,
+                                             int* misc) {
+  constexpr int NCH = EPT / 4;
+  const int tid = threadIdx.x;
+  const RowInfo cur = row_info(a, t);
+  const int cand = cur.cand;
+  uint32_t key[EPT];   // 0: no candidate
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.scores + (long long)t * a.stride, cand * 4);
+#pragma unroll
+  for (int e = 0; e < NCH; ++e) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rr, (e * NT + tid) * 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = f2u(u2f(v[j]) + 0.0f);   // -0 + 0 = +0
+      const uint32_t k = x ^ ((uint32_t)((int)x >> 31) | 0x80000000u);
+      key[4 * e + j] = 4 * (e * NT + tid) + j < cand ? k : 0u;
+    }
+  }
+  __syncthreads();   // the previous row's LDS contents are dead
+  fallback_keys<NT, EPT>(a, cur, key, sel, hist, wsum, misc);
+}
+
+// Rows the fast kernel left (negative length): a fixed grid of workgroups, each reading the
+// flags of 64 of its rows at a time (rows blockIdx.x + i*gridDim.x) and processing flagged
+// rows one after the other.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_fallback_kernel(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  u64* sel = reinterpret_cast<u64*>(smem);                                   // [p2max]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);           // [kHistSlots]
+  int* wsum = reinterpret_cast<int*>(hist + kHistSlots);                     // [32]
+  int* misc = wsum + 32;                                                     // [8]
+  const int lane = threadIdx.x & 63;
+  const int G = gridDim.x;
+  for (int r0 = blockIdx.x; r0 < a.T; r0 += 64 * G) {
+    const int row = r0 + lane * G;
+    const bool flagged = row < a.T && a.out_lengths[row] < 0;
+    u64 m = __ballot(flagged);
+    __syncthreads();   // every wave has read the flags before any row's length is rewritten
+    while (m) {
+      const int i = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      fallback_row<NT, EPT>(a, __builtin_amdgcn_readfirstlane(r0 + i * G), sel, hist, wsum, misc);
+    }
+  }
+}
+
+// Launches kernel k (one of the two kernels at one shape) with `lds` bytes of dynamic LDS.
+// The dynamic LDS limit is raised only when a launch needs more than the default 64 KB, and
+// only to what it needs: the raised limit is what each workgroup reserves, so a blanket
+// 160 KB would leave one workgroup per CU. Done once per (kernel, device, size) and never
+// inside graph capture (it is not a stream operation).
+template <int NT>
+hipError_t launch_kernel(void (*k)(TopkArgs), const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
   if (lds > 64 * 1024) {
     static std::mutex mu;
+    static const void* fn_of[64] = {nullptr};
     static size_t set_to[64] = {0};
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(mu);
-    if (device >= 64 || set_to[device] != lds) {
-      e = hipFuncSetAttribute((const void*)topk_kernel<NT, EPT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (device >= 64 || set_to[device] != lds || fn_of[device] != (const void*)k) {
+      e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      if (device < 64) set_to[device] = lds;
+      if (device < 64) { set_to[device] = lds; fn_of[device] = (const void*)k; }
     }
   }
-  hipLaunchKernelGGL((topk_kernel<NT, EPT>), dim3(grid), dim3(NT), lds, st, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(NT), lds, st, a);
   return hipGetLastError();
+}
+
+template <int NT, int EPT>
+hipError_t launch_cfg(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
+  return launch_kernel<NT>(topk_kernel<NT, EPT>, a, lds, grid, st);
+}
+
+template <int NT, int EPT>
+hipError_t launch_fallback(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
+  return launch_kernel<NT>(topk_fallback_kernel<NT, EPT>, a, lds, grid, st);
 }
 
 int p2_of(int topk, int max_cand) {
@@ -906,7 +1017,19 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
     else e = launch_cfg<1024, 32>(a, lds, (int)grid, st);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  // Rows the bin kernels left (clustered or tied scores, no finite score range), found by
+  // their negative length: one launch over a fixed grid in the shape of the longest row.
+  a.cls_lo = 0; a.cls_hi = mc; a.cls_map = 0;
+  a.p2max = p2_of(p.topk, mc);
+  a.hist_off = topk_hist_offset(mc, p.topk);
+  const size_t lds = topk_lds_bytes(mc, p.topk);
+  const int grid = std::min(p.T, kFallbackGrid);
+  if (mc <= 1024) return launch_fallback<256, 4>(a, lds, grid, st);
+  if (mc <= 2048) return launch_fallback<256, 8>(a, lds, grid, st);
+  if (mc <= 4096) return launch_fallback<256, 16>(a, lds, grid, st);
+  if (mc <= 8192) return launch_fallback<256, 32>(a, lds, grid, st);
+  if (mc <= 16384) return launch_fallback<512, 32>(a, lds, grid, st);
+  return launch_fallback<1024, 32>(a, lds, grid, st);
 }
 
 }  // namespace dsa
