@@ -1,19 +1,20 @@
 // Per-row top-k selection over the score workspace, with KPool expansion (gfx950).
 //
 // One workgroup per query row. Each thread holds 4-candidate chunks of the row, interleaved
-// across the workgroup, as order-preserving uint32 keys in registers; chunk groups past the
-// row's last candidate are skipped by every pass. A 2048-bin histogram linear in the score
-// (LDS integer atomics) gives the bin holding the topk-th largest key, whose few keys are
-// then ranked exactly. Every candidate above that key is taken and, among candidates equal
-// to it, the lowest indices (deterministic tie breaking, Megatron-LM PR 5992, "Key
-// changes"). The same bins order the selection: bin starts come from the histogram's suffix
-// sums, every selected candidate goes to its bin's range, and its exact rank inside the bin
-// (score descending, index ascending) gives its output position. Rows whose bins do not
-// separate the scores (clustered or tied scores, outliers, no finite range) take an
-// 11 + 11 + 10-bit radix select, a compaction by block prefix sums and a bitonic network.
-// The kernel uses no floating-point atomics and its result does not depend on scheduling.
-// Outputs are padded with -1 / -inf. For KPool (PR 7522, "Changes") selected pools are
-// expanded to their tokens and the query's incomplete causal pool is appended when requested.
+// across the workgroup, in registers; chunk groups past the row's last candidate are skipped
+// by every pass. A 2048-bin histogram linear in the score (LDS integer atomics) gives the bin
+// holding the topk-th largest key, whose few keys are then ranked exactly. Every candidate
+// above that key is taken and, among candidates equal to it, the lowest indices
+// (deterministic tie breaking, Megatron-LM PR 5992, "Key changes"). The same bins order the
+// selection: bin starts come from the histogram's suffix sums, every selected candidate goes
+// to its bin's range, and its exact rank inside the bin (score descending, index ascending)
+// gives its output position. Rows whose bins do not separate the scores (clustered or tied
+// scores, outliers, no finite range) are finished by a second kernel: an 11 + 11 + 10-bit
+// radix select, a compaction by block prefix sums and a bitonic network. Rows longer than
+// 4096 candidates run in launch shapes sized to them. No floating-point atomics; the result
+// does not depend on scheduling. Outputs are padded with -1 / -inf. For KPool (PR 7522,
+// "Changes") selected pools are expanded to their tokens and the query's incomplete causal
+// pool is appended when requested.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
