@@ -101,16 +101,32 @@ __device__ __forceinline__ void load_f32(const float* p, float (&x)[N]) {
   }
 }
 
-// One (t, h) query vector per group of D/NE lanes; lane g owns elements NE*g .. NE*g+NE-1.
+// One (t, h) query vector per D/NE lanes; the lane of part g owns elements NE*g .. NE*g+NE-1.
 // With rotate-half RoPE a lane's elements must rotate together: NE divides rope_dim/2.
+// A block's VPB vectors are split by part: the threads first hold the parts that RoPE
+// touches (the last nr parts of every vector), then the others, so that whole waves either
+// rotate or not (a wave with both kinds would run both code paths). The scale's magnitude
+// maximum then spans waves: it is combined with LDS integer atomics.
 template <int D, bool IN_BF16, int PREC, int NE>
 __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
   constexpr int G = D / NE;                      // lanes per vector
   constexpr int VPB = 256 / G;                   // vectors per block
-  const int g = threadIdx.x % G;
-  const long long v = (long long)block * VPB + threadIdx.x / G;
+  constexpr int NS = PREC == kPrecFP8 ? 1 : D / 32;   // scales per vector
+  __shared__ uint32_t amax_s[PREC == kPrecBF16 ? 1 : VPB * NS];
+  const int nr = a.R > 0 ? G - (D - a.R) / NE : 0;    // parts per vector with rotated elements
+  const int tau = threadIdx.x;
+  int vb, g;                                     // vector within the block, part
+  if (tau < VPB * nr) {
+    vb = tau / nr;
+    g = G - nr + tau % nr;
+  } else {
+    vb = (tau - VPB * nr) / (G - nr);
+    g = (tau - VPB * nr) % (G - nr);
+  }
   const long long nvec = (long long)a.T * a.H;
-  if (v >= nvec) return;                         // no cross-lane work below spans vectors
+  const long long v_raw = (long long)block * VPB + vb;
+  const bool valid = v_raw < nvec;
+  const long long v = valid ? v_raw : 0;         // past the end: vector 0 is read, nothing stored
   const int t = (int)(v / a.H);
   const long long base = v * D + NE * g;
   const int e0 = NE * g;                         // first element of this lane
@@ -168,7 +184,7 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
     }
   }
 
-  if (a.q_f32) {
+  if (a.q_f32 && valid) {
     float4* o = reinterpret_cast<float4*>(a.q_f32 + base);
 #pragma unroll
     for (int c = 0; c < NE / 4; ++c) o[c] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
@@ -180,30 +196,30 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
     for (int j = 0; j < NE / 2; ++j)
       w[j] = (uint32_t)f32_to_bf16_rne(x[2 * j]) | ((uint32_t)f32_to_bf16_rne(x[2 * j + 1]) << 16);
     uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q_op) + base);
+    if (valid) {
 #pragma unroll
-    for (int c = 0; c < NE / 8; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
-  } else {
-    uint32_t w[NE / 4];
-    if (PREC == kPrecFP8) {
-      float amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < NE; ++j) amax = fmaxf(amax, fabsf(x[j]));
-      amax = group_amax<G>(amax);                // the vector's G lanes
-      const int e = ue8m0_exponent(amax);
-      e4m3_pack<NE>(x, e, w);
-      if (g == 0) a.q_scale[v] = (uint8_t)(e + 127);
-    } else {
-      float amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < NE; ++j) amax = fmaxf(amax, fabsf(x[j]));
-      amax = group_amax<32 / NE>(amax);          // the lanes of one 32-element block
-      const int e = ue8m0_exponent(amax);
-      e4m3_pack<NE>(x, e, w);
-      if (g % (32 / NE) == 0) a.q_scale[v * (D / 32) + g / (32 / NE)] = (uint8_t)(e + 127);
+      for (int c = 0; c < NE / 8; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
     }
-    uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.q_op) + base);
+  } else {
+    // magnitude maximum per scale block (the vector for FP8, 32 elements for MXFP8): lane
+    // maxima, combined in LDS (non-negative floats order like their bits)
+    const int slot = vb * NS + (NS == 1 ? 0 : e0 / 32);
+    for (int i = tau; i < VPB * NS; i += 256) amax_s[i] = 0u;
+    __syncthreads();
+    float amax = 0.f;
 #pragma unroll
-    for (int c = 0; c < NE / 16; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+    for (int j = 0; j < NE; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    atomicMax(&amax_s[slot], f2u(amax));
+    __syncthreads();
+    const int e = ue8m0_exponent(u2f(amax_s[slot]));
+    uint32_t w[NE / 4];
+    e4m3_pack<NE>(x, e, w);
+    if (valid) {
+      if (e0 % (NS == 1 ? D : 32) == 0) a.q_scale[v * NS + (NS == 1 ? 0 : e0 / 32)] = (uint8_t)(e + 127);
+      uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.q_op) + base);
+#pragma unroll
+      for (int c = 0; c < NE / 16; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+    }
   }
 }
 
