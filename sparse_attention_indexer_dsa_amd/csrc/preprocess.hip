@@ -27,6 +27,9 @@ struct PreArgs {
   int R, max_pos, interleaved, rope_fp32;
   void* q_op; uint8_t* q_scale; void* k_op; uint8_t* k_scale;
   float* q_f32; float* k_f32;
+  // query thread split (see preprocess_q): parts per vector with rotated elements, and
+  // ceil(2^16 / n) for n = nr and n = D/16 - nr (0 when n = 0): x / n = (x * m) >> 16 for x < 256
+  int q_nr, q_mul_r, q_mul_p;
 };
 
 __device__ __forceinline__ int token_position(const int32_t* cu, int B, int T, int t) {
@@ -113,15 +116,17 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
   constexpr int VPB = 256 / G;                   // vectors per block
   constexpr int NS = PREC == kPrecFP8 ? 1 : D / 32;   // scales per vector
   __shared__ uint32_t amax_s[PREC == kPrecBF16 ? 1 : VPB * NS];
-  const int nr = a.R > 0 ? G - (D - a.R) / NE : 0;    // parts per vector with rotated elements
+  static_assert(NE == 16, "the split factors are computed for 16 elements per lane");
+  const int nr = a.q_nr;                         // parts per vector with rotated elements
   const int tau = threadIdx.x;
   int vb, g;                                     // vector within the block, part
   if (tau < VPB * nr) {
-    vb = tau / nr;
-    g = G - nr + tau % nr;
+    vb = (tau * a.q_mul_r) >> 16;
+    g = G - nr + (tau - vb * nr);
   } else {
-    vb = (tau - VPB * nr) / (G - nr);
-    g = (tau - VPB * nr) % (G - nr);
+    const int x = tau - VPB * nr;
+    vb = (x * a.q_mul_p) >> 16;
+    g = x - vb * (G - nr);
   }
   const long long nvec = (long long)a.T * a.H;
   const long long v_raw = (long long)block * VPB + vb;
@@ -412,6 +417,12 @@ hipError_t launch_preprocess(const PreprocessLaunch& p, hipStream_t st) {
   a.R = p.rope_dim; a.max_pos = p.max_pos; a.interleaved = p.interleaved; a.rope_fp32 = p.rope_fp32;
   a.q_op = p.q_op; a.q_scale = p.q_scale; a.k_op = p.k_op; a.k_scale = p.k_scale;
   a.q_f32 = p.q_f32; a.k_f32 = p.k_f32;
+  {
+    const int G = p.D / 16;
+    a.q_nr = p.rope_dim > 0 ? G - (p.D - p.rope_dim) / 16 : 0;
+    a.q_mul_r = a.q_nr > 0 ? (65536 + a.q_nr - 1) / a.q_nr : 0;
+    a.q_mul_p = G - a.q_nr > 0 ? (65536 + (G - a.q_nr) - 1) / (G - a.q_nr) : 0;
+  }
   if (p.D == 128) return p.in_bf16 ? launch_pre_p<128, true>(a, p.precision, st) : launch_pre_p<128, false>(a, p.precision, st);
   return p.in_bf16 ? launch_pre_p<64, true>(a, p.precision, st) : launch_pre_p<64, false>(a, p.precision, st);
 }
