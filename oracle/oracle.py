@@ -32,6 +32,15 @@ runs them:
 7. ``expand``      - selected pools back to token indices, plus the query's
                      incomplete causal pool when the tail option is on
                      (PR 7522, "Changes").
+8. ``selection_softmax`` - the optional softmax over each row's selected scores,
+                     the indexer's predicted distribution that its loss reuses
+                     (PR 5992 reviews: "What was verified", the variable return
+                     arity of the top-k call with ``return_softmax``; "Areas
+                     checked and found clean", the loss restructure reusing the
+                     compact softmax). Reading: p_j = exp(s_j - m) / sum_i
+                     exp(s_i - m) over the row's selected scores, m their
+                     maximum; padding gets 0 and a row with nothing selected is
+                     all zeros; with KPool it runs over the selected pools.
 
 Everything is plain numpy; there is no blocking beyond splitting rows into
 groups so that one matmul fits in memory.
@@ -366,3 +375,22 @@ def dense_outputs(res, T, topk, kp=1):
         if kp > 1:
             tok[t, :r["tokens"].size] = r["tokens"]
     return idx, scr, lng, tok
+
+
+# --------------------------------------------------------------------------
+# 8. Softmax over the selection
+# --------------------------------------------------------------------------
+
+def selection_softmax(scores):
+    """Softmax over one row of selected scores (padding -inf): exp(s_j - m) / sum_i
+    exp(s_i - m) over the finite entries, m their maximum; padding entries get 0 and a
+    row without a finite entry is all zeros. float64."""
+    s = np.asarray(scores, dtype=F64)
+    out = np.zeros(s.shape, F64)
+    sel = s > -np.inf
+    if not sel.any():
+        return out
+    m = np.max(s[sel])
+    e = np.exp(s[sel] - m)
+    out[sel] = e / np.sum(e)
+    return out

@@ -262,3 +262,44 @@ def test_fp8_changes_selection():
         sel[p] = [frozenset(res[t]["sel"]) for t in range(256)]
     diff = sum(a != b for a, b in zip(sel["bf16"], sel["fp8"]))
     assert 0 < diff < 256
+
+
+# ---------------------------------------------------------------- selection softmax
+
+def test_selection_softmax_worked_values():
+    # scores 0, ln 2, ln 3: the exponentials are 1, 2, 3, so the softmax is 1/6, 2/6, 3/6
+    p = orc.selection_softmax([np.log(3.0), np.log(2.0), 0.0, -np.inf])
+    np.testing.assert_allclose(p, [0.5, 1 / 3, 1 / 6, 0.0], rtol=1e-14, atol=0)
+    assert p[3] == 0.0
+
+
+def test_selection_softmax_equal_scores_are_uniform():
+    for n in (1, 2, 4, 64, 2048):
+        p = orc.selection_softmax(np.full(n, 3.25))
+        assert np.all(p == 1.0 / n)          # exact: every exponential is 1
+
+
+def test_selection_softmax_two_scores_are_logistic():
+    rng = np.random.default_rng(5)
+    for a, b in rng.standard_normal((20, 2)) * 10:
+        p = orc.selection_softmax([a, b])
+        # the logistic function of the difference, written through tanh
+        assert abs(p[0] - 0.5 * (1.0 + np.tanh((a - b) / 2.0))) <= 1e-15
+
+
+def test_selection_softmax_invariants():
+    rng = np.random.default_rng(6)
+    s = np.sort(rng.standard_normal(300) * 4)[::-1]
+    s = np.concatenate([s, np.full(212, -np.inf)])
+    p = orc.selection_softmax(s)
+    assert abs(np.sum(p) - 1.0) <= 1e-13
+    assert np.all(p[300:] == 0.0) and np.all(p[:300] > 0.0)
+    assert np.all(np.diff(p[:300]) <= 0)                 # descending scores, descending weights
+    np.testing.assert_allclose(orc.selection_softmax(s + 7.5), p, rtol=1e-12)   # shift invariance
+    # ratio of two weights is the exponential of the score difference
+    assert abs(p[0] / p[1] - np.exp(s[0] - s[1])) <= 1e-12 * np.exp(s[0] - s[1])
+
+
+def test_selection_softmax_empty_row():
+    assert np.all(orc.selection_softmax(np.full(16, -np.inf)) == 0.0)
+    assert orc.selection_softmax(np.zeros(0)).size == 0
