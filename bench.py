@@ -60,7 +60,7 @@ def pair_count(cu, kp):
     return tot
 
 
-def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False):
+def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False):
     import torch
     import sparse_attention_indexer_dsa_amd as dsa
     import parity
@@ -95,6 +95,7 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False):
             pool["pooled_scale"] = torch.empty((P,) if prec == "fp8" else (P, nsb), dtype=torch.uint8, device=dev)
     ws = torch.empty(dsa.workspace_size(T, max_seqlen, topk, kp, H, D, B, prec), dtype=torch.uint8, device=dev)
     outs = dsa._alloc_outputs(None, T, topk, kp, dev)
+    sm_out = torch.empty((T, topk), dtype=torch.float32, device=dev) if softmax else None
     k_op = pool["pooled_op"] if kp > 1 else (ops["k_op"] if inp["preprocess"] else d["k"])
     k_scale = pool.get("pooled_scale") if kp > 1 else ops.get("k_scale")
 
@@ -128,6 +129,10 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False):
                  out=outs)
         if ev is not None:
             ev[i].record(); i += 1
+        if softmax:
+            dsa.selection_softmax(outs["scores"], out=sm_out)
+        if ev is not None:
+            ev[i].record(); i += 1
 
     for _ in range(warmup):
         step()
@@ -153,7 +158,7 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False):
     # Per-kernel durations: the same steps run eagerly with HIP events around every library
     # call on the stream the kernels run on, queued behind a spin kernel so that the stream
     # never waits for the host between a kernel and its events.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda._sleep(20_000_000)
     for s in range(steps):
         step(events[s])
@@ -165,7 +170,7 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False):
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-    names = ["preprocess", "kpool", "score", "topk"]
+    names = ["preprocess", "kpool", "score", "topk", "softmax"]
     per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])) / 1e3
            for i, n in enumerate(names)}
     return (t1 - t0), per, fused
@@ -188,6 +193,7 @@ def algorithmic(inp, pairs, fused):
         out["kpool_bytes"] = float(T * D * 2 + T * 2 + P * D * esz)
     width = topk if kp == 1 else topk * kp + kp - 1
     out["topk_bytes"] = float(pairs * 4 + T * topk * 4 + T * width * 4 + T * 4 + (T * topk * 4 if kp > 1 else 0))
+    out["softmax_bytes"] = float(2 * T * topk * 4)     # the selected scores in, the weights out
     q_bytes = T * H * D * 2 if fused else T * H * D * esz + T * H * nsb
     out["score_bytes"] = float(q_bytes + T * H * 4 + (T // kp) * D * esz + pairs * 4)
     return out
@@ -284,6 +290,9 @@ def main():
     ap.add_argument("--fuse", action="store_true",
                     help="preprocess the queries inside the scoring kernel (dsa_index_score_fused) instead of in "
                          "the preprocessing kernel")
+    ap.add_argument("--softmax", action="store_true",
+                    help="also compute the softmax over each row's selection (dsa_index_selection_softmax) in "
+                         "every step")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="record scoring-kernel traffic from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
@@ -302,12 +311,13 @@ def main():
     kp = inp["kpool"]
     pairs = pair_count(inp["cu_seqlens"], kp)
     print(f"[bench] workload {args.workload}: {inp['name']} T={T} pairs={pairs}", file=sys.stderr, flush=True)
-    elapsed, per, fused = run_gpu(inp, args.steps, args.warmup, args.copy_mb, args.fuse)
+    elapsed, per, fused = run_gpu(inp, args.steps, args.warmup, args.copy_mb, args.fuse, args.softmax)
     alg = algorithmic(inp, pairs, fused)
     prec = inp["precision"]
     kernels = {}
-    for n in ("preprocess", "kpool", "score", "topk"):
-        if per[n] <= 0 or (n == "preprocess" and not inp["preprocess"]) or (n == "kpool" and kp == 1):
+    for n in ("preprocess", "kpool", "score", "topk", "softmax"):
+        if per[n] <= 0 or (n == "preprocess" and not inp["preprocess"]) or (n == "kpool" and kp == 1) or \
+                (n == "softmax" and not args.softmax):
             continue
         k = {"ms": round(per[n] * 1e3, 4)}
         if n == "score":
@@ -341,6 +351,7 @@ def main():
                    else f"{len(inp['docs'])} docs", "topk": inp["topk"], "kpool": kp, "precision": prec,
                    "preprocess": bool(inp["preprocess"]), "query_preprocessing": "in the scoring kernel" if fused
                    else ("own kernel" if inp["preprocess"] else "none"), "pairs_per_step": pairs,
+                   "selection_softmax": bool(args.softmax),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "score", "achieved": round(achieved, 2),
                      "peak": PEAK_FLOPS[prec] / 1e12, "unit": "TFLOP/s",

@@ -298,6 +298,23 @@ dsa_status_t dsa_index_forward(
     void* q_op_out, uint8_t* q_scale_out,
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * dsa_index_selection_softmax - softmax over each row's selected scores: the optional third
+ * output of the indexer's top-k, the predicted distribution that the indexer loss reuses
+ * (Megatron-LM PR 5992 reviews: "What was verified", the top-k call's return arity with
+ * return_softmax; "Areas checked and found clean", the loss reusing the compact softmax).
+ * For row t: out[t,j] = exp(s_j - m) / sum_i exp(s_i - m) with s = scores[t, 0..topk) and m
+ * the row's maximum; -inf entries (the padding of the top-k outputs) get 0, and a row with
+ * no finite entry is all zeros. With KPool it runs over the selected pools' scores.
+ *   scores   [T, topk] fp32, DEVICE, 4-byte aligned: out_scores of a top-k call.
+ *   out      [T, topk] fp32, DEVICE, 4-byte aligned, caller-owned; may be `scores` itself.
+ * Arithmetic: fp32, expf, one division per entry; per-row sums in a fixed order (results do
+ * not depend on scheduling). Errors: DSA_ERR_INVALID_ARGUMENT for T < 0, topk < 1, NULL or
+ * misaligned pointers (T > 0); DSA_ERR_DEVICE if the launch fails.
+ */
+dsa_status_t dsa_index_selection_softmax(const float* scores, int32_t T, int32_t topk, float* out,
+                                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "score_fused", "topk", "forward",
-           "forward_workspace_size", "library_path", "load", "PRECISIONS", "DsaError"]
+           "forward_workspace_size", "selection_softmax", "library_path", "load", "PRECISIONS", "DsaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libdsa_index.so"
@@ -75,6 +75,8 @@ def load():
     lib.dsa_index_forward.restype = i32
     lib.dsa_index_forward.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, i32, i32, vp, vp, f32, vp, vp,
                                       i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_index_selection_softmax.restype = i32
+    lib.dsa_index_selection_softmax.argtypes = [vp, i32, i32, vp, vp]
     lib.dsa_index_score_fused.restype = i32
     lib.dsa_index_score_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32,
                                           i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
@@ -381,3 +383,22 @@ def topk(workspace, T, cu_seqlens, max_seqlen, topk, *, kpool=1, cu_pools=None, 
         _stream(workspace.device))
     _check(st, "dsa_index_topk")
     return out
+
+
+def selection_softmax(scores, *, out=None):
+    """Softmax over each row of top-k scores ([T, topk] fp32, padding -inf): exp(s - max) / sum,
+    padding 0, empty rows all zeros. ``out`` may be ``scores`` itself."""
+    lib = load()
+    _need(scores, "scores", (torch.float32,))
+    if scores.dim() != 2:
+        raise ValueError(f"scores must be [T, topk], got shape {tuple(scores.shape)}")
+    if out is None:
+        out = torch.empty_like(scores)
+    _need(out, "out", (torch.float32,), device=scores.device)
+    if out.shape != scores.shape:
+        raise ValueError(f"out shape {tuple(out.shape)} differs from scores {tuple(scores.shape)}")
+    T, k = scores.shape
+    st = lib.dsa_index_selection_softmax(_ptr(scores), int(T), int(k), _ptr(out), _stream(scores.device))
+    _check(st, "dsa_index_selection_softmax")
+    return out
+

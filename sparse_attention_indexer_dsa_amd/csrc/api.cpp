@@ -459,4 +459,15 @@ dsa_status_t dsa_index_forward(
   return DSA_OK;
 }
 
+dsa_status_t dsa_index_selection_softmax(const float* scores, int32_t T, int32_t topk, float* out,
+                                         hipStream_t stream) {
+  if (T < 0 || topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "need T >= 0 and topk >= 1 (T=%d, topk=%d)", T, topk);
+  if (T == 0) return DSA_OK;
+  if (!scores || !out) return fail(DSA_ERR_INVALID_ARGUMENT, "scores and out must not be NULL");
+  if (!aligned(scores, 4) || !aligned(out, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "scores and out must be 4-byte aligned");
+  hipError_t e = dsa::launch_selection_softmax(scores, T, topk, out, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_selection_softmax");
+  return DSA_OK;
+}
+
 }  // extern "C"

@@ -57,6 +57,8 @@ bool score_can_fuse_rope(int precision, int rope_dim, int interleaved);
 hipError_t launch_score(const ScoreTopkLaunch& p, hipStream_t st);
 hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st);
 
+hipError_t launch_selection_softmax(const float* scores, int T, int topk, float* out, hipStream_t st);
+
 // Largest row (candidates) the LDS top-k supports.
 constexpr int kTopkMaxCand = 32768;
 

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
     assert {"dsa_index_preprocess", "dsa_index_kpool", "dsa_index_workspace_size", "dsa_index_score_topk",
             "dsa_index_score", "dsa_index_topk", "dsa_index_forward", "dsa_index_forward_workspace_size",
-            "dsa_index_score_fused",
+            "dsa_index_score_fused", "dsa_index_selection_softmax",
             "dsa_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -163,6 +163,17 @@ def test_kpool_validation(lib):
     assert f(FAKE, 0, 64, 100, FAKE, 1, FAKE, FAKE, 4, 0, FAKE, None, FAKE, None) == 2
     assert f(FAKE, 0, 64, 128, None, 1, FAKE, FAKE, 4, 0, FAKE, None, FAKE, None) == 1
     assert f(FAKE, 0, 64, 128, FAKE, 1, FAKE, FAKE, 4, 1, FAKE, None, FAKE, None) == 1   # fp8 needs scales
+
+
+def test_selection_softmax_validation(lib):
+    f = lib.dsa_index_selection_softmax
+    assert f(FAKE, -1, 8, FAKE, None) == 1
+    assert f(FAKE, 4, 0, FAKE, None) == 1
+    assert f(None, 4, 8, FAKE, None) == 1
+    assert f(FAKE, 4, 8, None, None) == 1
+    assert f(FAKE + 2, 4, 8, FAKE, None) == 1               # misaligned
+    assert b"aligned" in lib.dsa_last_error()
+    assert f(None, 0, 8, None, None) == 0                   # empty problem: nothing to do
 
 
 def test_python_binding_maps_errors():
