@@ -330,7 +330,7 @@ __device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* w
 constexpr int kValueList = 64;   // a threshold bin this small is resolved by counting
 constexpr int kBucketMax = 64;   // a selected pass-1 bin larger than this: bitonic ordering instead
 constexpr int kHistSlots = 2048 + 16;   // pass-1 bins, then a slot that counts non-candidates
-constexpr int kFallbackGrid = 256;      // workgroups of the fallback launch
+constexpr int kFallbackGrid = 1024;     // workgroups of the fallback launch
 
 struct RowInfo {
   int t, b, lo, u, cand, nsel;
@@ -569,30 +569,24 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       uint32_t* list = reinterpret_cast<uint32_t*>(selA);
       {
         uint32_t hit = 0;   // bit 4e+j: candidate in bin d1
-        int mine = 0;
 #pragma unroll
         for (int e = 0; e < NCH; ++e)
           if (live(e)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bool h = cand_at(e, j) && binat(e, j) == d1;
-              hit |= (uint32_t)h << (4 * e + j);
-              mine += h;
-            }
+            for (int j = 0; j < 4; ++j) hit |= (uint32_t)(cand_at(e, j) && binat(e, j) == d1) << (4 * e + j);
           }
+        const int mine = __builtin_popcount(hit);
         const int incl = wave_prefix_sum(mine);
         const int wtot = __builtin_amdgcn_readlane(incl, 63);
         int base = 0;
         if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&misc[5], wtot);
         int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
-        if (hit) {
-#pragma unroll
-          for (int e = 0; e < NCH; ++e)
-            if (live(e)) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if ((hit >> (4 * e + j)) & 1u) list[pos++] = keyat(e, j);
-            }
+        // the few hits, by their set bits; the key is recomputed from the row (in the cache)
+        const float* row = a.scores + (long long)t * a.stride;
+        while (hit) {
+          const int bpos = __builtin_ctz(hit);   // 4e + j
+          hit &= hit - 1;
+          list[pos++] = keyof(row[4 * ((bpos >> 2) * NT + tid) + (bpos & 3)] + 0.0f);
         }
       }
       __syncthreads();
