@@ -328,7 +328,13 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
   typedef AOperand<PREC> AType;
   AType aop[2][KSTEPS];
   int asc[2][KSTEPS];
+  // The per-row weights: in registers, or (bf16 operands with 64 heads, where the resident
+  // q operands already take 64 registers) in LDS, read as four broadcast 16-byte loads per
+  // 32-row block in the epilogue, which keeps the kernel within 256 registers without spills
+  // (the fused variant keeps them in registers: its prologue needs the LDS reads' registers).
+  constexpr bool kWLds = !kFP8 && H == 64 && !FUSE;
   float wl[2][16];
+  __shared__ __attribute__((aligned(16))) float w_lds[kWLds ? 4 * 64 : 1];
   if (FUSE) {
     // one operand row at a time (each holds 64 fp32 values while it is being built)
 #pragma unroll
@@ -376,8 +382,10 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
         wv_ = a.w_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.w)[wi]) : reinterpret_cast<const float*>(a.w)[wi];
       }
       wl[rb][i] = wv_;
+      if (kWLds && col < 4 && (i % 4) == col) w_lds[wv * 64 + rr] = wv_;   // each row once
     }
   }
+  if (kWLds) __syncthreads();
 
   // candidates of the tokens this lane writes (see the epilogue)
   int cand_tok[4];
@@ -476,7 +484,18 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wl[rb][i], relu(acc[rb][i]), s);
+        for (int g = 0; g < 4; ++g) {
+          float w4[4];
+          if (kWLds) {
+            const float4 q = *reinterpret_cast<const float4*>(w_lds + wv * 64 + rb * 32 + g * 8 + hl * 4);
+            w4[0] = q.x; w4[1] = q.y; w4[2] = q.z; w4[3] = q.w;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w4[k] = wl[rb][4 * g + k];
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) s = __builtin_fmaf(w4[k], relu(acc[rb][4 * g + k]), s);
+        }
       s = pair_sum(s) * a.sm_scale;
       const uint32_t off = (hl == 0 && (uint32_t)c < (uint32_t)cand_tok[0]) ? (uint32_t)c * 4u : kDrop;
       __builtin_amdgcn_raw_buffer_store_b32(f2u(s), out_r, off, 0, 0);
