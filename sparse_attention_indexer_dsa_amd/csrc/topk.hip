@@ -265,10 +265,12 @@ __device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int krem, in
 // The same search over the 2048 pass-1 bins, which then replaces every bin's count c by
 // (above(d) << 16) | c: above(d) is the first output slot of bin d (counts and slots are at
 // most 32768, so both fields fit). Sets misc[6] (zeroed by the caller) when a thread owning
-// a bin at or above the found one has a bin of more than `heavy` keys. Only the thread whose
-// bins hold the rank scans them one by one.
+// a bin at or above the found one has a bin of more than `heavy` keys, and misc[8] (set to
+// 2047 by the caller) to the bin holding the rank2-th largest key when there is one. Only
+// the thread whose bins hold a rank scans them one by one.
 template <int NT>
-__device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* wsum, int* misc, int heavy) {
+__device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* wsum, int* misc, int heavy,
+                                                int rank2) {
   constexpr int NW = NT / 64;
   constexpr int PER = 2048 / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -322,6 +324,13 @@ __device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* w
     for (int j = PER - 1; j >= 0; --j) {
       const int a0 = (int)st[j], hc = (int)h[j];
       if (a0 < krem && krem <= a0 + hc) { misc[0] = tid * PER + j; misc[1] = a0; misc[2] = hc; }
+    }
+  }
+  if (above < rank2 && rank2 <= above + mine) {
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      const int a0 = (int)st[j], hc = (int)h[j];
+      if (a0 < rank2 && rank2 <= a0 + hc) misc[8] = tid * PER + j;
     }
   }
   __syncthreads();
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   u64* selA = reinterpret_cast<u64*>(smem);                                  // [p2max]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);           // [kHistSlots]
   int* wsum = reinterpret_cast<int*>(hist + kHistSlots);                     // [32]
-  int* misc = wsum + 32;                                                     // [8]
+  int* misc = wsum + 32;                                                     // [16]
 
   const int tid = threadIdx.x;
   const int topk = a.topk;
@@ -522,8 +531,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   const bool finite = span > 0.f && span < INFINITY;   // every candidate score finite, not all equal
   const float vscale = finite ? 2048.f / span : 0.f;
   const float voff = -vmin * vscale;
-  // pass-1 bin: (v - vmin) * 2048 / span as one fma (any rounding keeps the bins monotone in v)
-  auto binof = [&](float x) { return min(2047, max(0, (int)__builtin_fmaf(x, vscale, voff))); };
+  // First-level bin: (v - vmin) * 2048 / span as one fma (any rounding keeps the bins
+  // monotone in v). Second level (rows the first does not separate): the candidates of
+  // first-level bins >= dex, over [lo2, hi2], those above hi2 clamped into the top bin; the
+  // others get a spare slot.
+  int lvl = 0, dex = 0;
+  float vscale2 = 0.f, voff2 = 0.f;
+  auto bin1 = [&](float x) { return min(2047, max(0, (int)__builtin_fmaf(x, vscale, voff))); };
+  auto bin2 = [&](float x) { return min(2047, max(0, (int)__builtin_fmaf(x, vscale2, voff2))); };
+  auto binof = [&](float x) {
+    if (lvl == 0) return bin1(x);
+    return bin1(x) >= dex ? bin2(x) : 2048 + (int)(threadIdx.x & 15);
+  };
   // Accessors over the two register layouts. With KEEP, slots past the row carry key 0 and a
   // bin of 2048 or more, so no comparison below selects them without the `in` test.
   auto keyat = [&](int e, int j) {
@@ -535,29 +554,75 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   auto cand_at = [&](int e, int j) {
     if constexpr (KEEP) return true; else return in(e, j);
   };
-  if (finite) {
-    // ---- pass 1: 2048 bins linear in the score over [vmin, vmax]. Bins are monotone in the
+  auto run_pass = [&](int pass) {
+    // ---- pass: 2048 bins linear in the score over [vmin, vmax]. Bins are monotone in the
     //      score, and a smooth score distribution spreads evenly over them, so the LDS
     //      atomics rarely collide and the threshold bin holds few candidates. The same bins
     //      then order the selection: bins at and above the threshold bin, taken from the
     //      top, are the selection in descending order up to the order inside each bin.
     //      Slots past the row count in 2048..2063 (spread over banks so that their atomics
-    //      do not serialise on one address).
+    //      do not serialise on one address). A row the first level does not separate (a
+    //      crowded threshold bin or selected bin, typically because a few outlying scores
+    //      stretch [vmin, vmax]) is binned again, its candidates in first-level bins below
+    //      the threshold bin left out, over the exact range from the smallest remaining
+    //      score to the largest score in bins up to the 17th largest's; the at most 16
+    //      scores above that go to the top bin.
+    if (pass == 1) {
+      // the second range, from exact keys: the smallest score in first-level bins >= d1
+      // and the largest in bins <= the 17th largest's bin
+      const int dstar = misc[8];
+      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+      for (int e = 0; e < NCH; ++e)
+        if (live(e)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (in(e, j)) {
+              int b1;
+              if constexpr (KEEP) b1 = binA[4 * e + j]; else b1 = bin1(val[4 * e + j]);
+              const uint32_t k = keyat(e, j);
+              if (b1 >= d1) kmn = min(kmn, k);
+              if (b1 <= dstar) kmx = max(kmx, k);
+            }
+        }
+      block_minmax<NT>(kmn, kmx, wsum);
+      if (kmn == 0xFFFFFFFFu || kmx == 0u) return;
+      const float lo2 = key_score(kmn), hi2 = key_score(kmx);
+      const float span2 = hi2 - lo2;
+      if (!(span2 > 0.f && span2 < INFINITY)) return;
+      dex = d1;
+      vscale2 = 2048.f / span2;
+      voff2 = -lo2 * vscale2;
+      if (!(vscale2 < INFINITY) || !(fabsf(voff2) < INFINITY)) return;
+      lvl = 1;
+      __syncthreads();   // every thread has read misc and wsum above
+    }
+    resolved = cand <= topk;
+    thr = kmin;
+    krem = cand;
+    neq = 0;
     for (int i = tid; i < kHistSlots / 4; i += NT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid == 0) { misc[5] = 0; misc[6] = 0; }
+    if (tid == 0) { misc[5] = 0; misc[6] = 0; misc[8] = 2047; }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < NCH; ++e)
       if (live(e)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int d = in(e, j) ? binof(val[4 * e + j]) : 2048 + (tid & 15);
+          int d = 2048 + (tid & 15);
+          if (in(e, j)) {
+            // with KEEP the second level takes the score from its key (exact, -0 already
+            // folded), so the scores need not stay in registers past the first pass
+            if constexpr (KEEP) d = lvl == 0 ? bin1(val[4 * e + j])
+                                             : (binA[4 * e + j] >= dex ? bin2(key_score(keyA[4 * e + j])) : d);
+            else d = binof(val[4 * e + j]);
+          }
           if constexpr (KEEP) binA[4 * e + j] = d;
           atomicAdd(&hist[d], 1u);
         }
       }
     __syncthreads();
-    scan_pass1_bins<NT>(hist, nsel, wsum, misc, kBucketMax);
+    scan_pass1_bins<NT>(hist, nsel, wsum, misc, kBucketMax, 17);
     d1 = misc[0];
     a1 = misc[1];
     const int c1 = misc[2];
@@ -613,7 +678,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       resolved = true;
     }
     fast = resolved && !heavy;
-  }
+  };
+  if (finite) run_pass(0);
+  if (finite && !fast) run_pass(1);
 
   if (fast) {
     // ---- selection straight into bin order: bin d holds its candidates from slot
@@ -901,7 +968,7 @@ __global__ __launch_bounds__(NT) void topk_fallback_kernel(TopkArgs a) {
   u64* sel = reinterpret_cast<u64*>(smem);                                   // [p2max]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);           // [kHistSlots]
   int* wsum = reinterpret_cast<int*>(hist + kHistSlots);                     // [32]
-  int* misc = wsum + 32;                                                     // [8]
+  int* misc = wsum + 32;                                                     // [16]
   const int lane = threadIdx.x & 63;
   const int G = gridDim.x;
   for (int r0 = blockIdx.x; r0 < a.T; r0 += 64 * G) {
@@ -960,11 +1027,11 @@ int p2_of(int topk, int max_cand) {
 
 }  // namespace
 
-// Dynamic LDS layout: selA [p2max] u64 | hist [kHistSlots] u32 | wsum [32] | misc [8].
+// Dynamic LDS layout: selA [p2max] u64 | hist [kHistSlots] u32 | wsum [32] | misc [16].
 int topk_hist_offset(int max_cand, int topk) { return p2_of(topk, max_cand) * 8; }
 
 size_t topk_lds_bytes(int max_cand, int topk) {
-  return (size_t)topk_hist_offset(max_cand, topk) + kHistSlots * 4 + 32 * 4 + 8 * 4;
+  return (size_t)topk_hist_offset(max_cand, topk) + kHistSlots * 4 + 32 * 4 + 16 * 4;
 }
 
 hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {

@@ -153,3 +153,36 @@ def test_selection_many_documents(kp):
     docs[[3, 17, 40]] = 0
     docs[[5, 66]] = [9000, 5000] if kp == 1 else [20000, 36000]
     _run(docs, 256, kp, True, 80 + kp)
+
+
+@pytest.mark.parametrize("L, topk, big", [(4096, 512, 3000.0), (4096, 512, 1e30), (6000, 2048, 1e4),
+                                          (1500, 2048, 1e6)])
+def test_selection_outlier_rows(L, topk, big):
+    # every row has one outlying score (an attention-sink-like key), some also a low one:
+    # the linear bins over [min, max] crowd the rest into a few bins, and the kernel bins the
+    # selected region again
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    rng = np.random.default_rng(int(L + topk + np.log10(big)))
+    stride = (L + 63) // 64 * 64
+    gen_t = torch.Generator(device="cuda").manual_seed(L + topk)
+    flat = torch.randn(L * stride + 64, generator=gen_t, device="cuda", dtype=torch.float32) * 3.0
+    ws = flat[:L * stride].view(L, stride)
+    t_idx = torch.arange(L, device="cuda")
+    pos = torch.as_tensor(rng.integers(0, 1 << 30, L), device="cuda") % (t_idx + 1)
+    ws[t_idx, pos] = big
+    low = t_idx[t_idx % 5 == 0]
+    ws[low, low // 3] = -big
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    out = dsa.topk(flat, L, cu, L, topk)
+    torch.cuda.synchronize()
+    host = {n: out[n].cpu().numpy() for n in out}
+    cand = np.arange(L) + 1
+    assert np.array_equal(host["lengths"], np.minimum(topk, cand))
+    rows = sorted(set(int(x) for x in rng.choice(L, size=60, replace=False)) | set(range(L - 5, L)))
+    for t in rows:
+        v = ws[t, :t + 1].cpu().numpy().astype(np.float64)
+        sel, s = orc.topk_row(v, topk)
+        n = sel.size
+        assert np.array_equal(host["indices"][t][:n].astype(np.int64), sel), t
+        assert np.array_equal(host["scores"][t][:n].astype(np.float64), s), t
