@@ -8,9 +8,11 @@
 // (deterministic tie breaking, Megatron-LM PR 5992, "Key changes"). The same bins order the
 // selection: bin starts come from the histogram's suffix sums, every selected candidate goes
 // to its bin's range, and its exact rank inside the bin (score descending, index ascending)
-// gives its output position. Rows whose bins do not separate the scores (clustered or tied
-// scores, outliers, no finite range) are finished by a second kernel: an 11 + 11 + 10-bit
-// radix select, a compaction by block prefix sums and a bitonic network. Rows longer than
+// gives its output position. A row whose bins do not separate the scores (a few outliers
+// stretching the range) is binned again over its selected region; rows neither level
+// separates (clustered or tied scores, no finite range) are finished by a second kernel: an
+// 11 + 11 + 10-bit radix select, a compaction by block prefix sums and a bitonic network.
+// Rows longer than
 // 4096 candidates run in launch shapes sized to them. No floating-point atomics; the result
 // does not depend on scheduling. Outputs are padded with -1 / -inf. For KPool (PR 7522,
 // "Changes") selected pools are expanded to their tokens and the query's incomplete causal
