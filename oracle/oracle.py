@@ -41,6 +41,18 @@ runs them:
                      exp(s_i - m) over the row's selected scores, m their
                      maximum; padding gets 0 and a row with nothing selected is
                      all zeros; with KPool it runs over the selected pools.
+9. ``sparse_attention`` - the consumer of the selection: absorbed-MLA attention of
+                     each query head over the key/value entries the row selects
+                     (PR 8403, "Fused Path": FlashMLA sparse attention after the
+                     indexer, compressed KV of width 576 = kv_lora_rank 512 + 64;
+                     codex review finding 1: value width 512, invalid slots and
+                     supplied lengths). Reading: one latent entry per token serves
+                     every head; the key is the whole entry, the value its first
+                     512 elements; the selected entries are the row's first
+                     length[t] slots whose index is a valid token (-1 marks an
+                     empty slot); softmax over sm_scale * q . k of those entries,
+                     each slot counted once; a row with nothing selected gives
+                     zeros and log-sum-exp -inf.
 
 Everything is plain numpy; there is no blocking beyond splitting rows into
 groups so that one matmul fits in memory.
@@ -394,3 +406,40 @@ def selection_softmax(scores):
     e = np.exp(s[sel] - m)
     out[sel] = e / np.sum(e)
     return out
+
+
+# --------------------------------------------------------------------------
+# 9. Sparse attention over the selection
+# --------------------------------------------------------------------------
+
+def sparse_attention(q, kv, indices, sm_scale, dv=512, lengths=None):
+    """Absorbed-MLA attention over selected entries, float64.
+
+    q [T, H, Dk], kv [S, Dk] (one entry per token, shared by the heads), indices [T, K]
+    (token index or -1), lengths [T] or None (= K). For row t the selected entries are the
+    slots j < lengths[t] with 0 <= indices[t, j] < S. Returns out [T, H, dv], the
+    softmax(sm_scale * q[t, h] . kv[j]) weighted sum of kv[j, :dv], and lse [T, H], the
+    natural log of sum_j exp(sm_scale * q[t, h] . kv[j]) (-inf and a zero row when nothing
+    is selected)."""
+    q = np.asarray(q, dtype=F64)
+    kv = np.asarray(kv, dtype=F64)
+    idx = np.asarray(indices, dtype=np.int64)
+    T, H, _ = q.shape
+    S = kv.shape[0]
+    K = idx.shape[1] if idx.ndim == 2 else 0
+    out = np.zeros((T, H, dv), F64)
+    lse = np.full((T, H), -np.inf, F64)
+    for t in range(T):
+        n = K if lengths is None else max(0, min(int(lengths[t]), K))
+        row = idx[t, :n]
+        sel = row[(row >= 0) & (row < S)]
+        if sel.size == 0:
+            continue
+        ent = kv[sel]                                  # [n, Dk]
+        s = sm_scale * (q[t] @ ent.T)                  # [H, n]
+        m = np.max(s, axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = np.sum(e, axis=1, keepdims=True)
+        out[t] = (e @ ent[:, :dv]) / z
+        lse[t] = (m + np.log(z))[:, 0]
+    return out, lse

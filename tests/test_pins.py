@@ -303,3 +303,119 @@ def test_selection_softmax_invariants():
 def test_selection_softmax_empty_row():
     assert np.all(orc.selection_softmax(np.full(16, -np.inf)) == 0.0)
     assert orc.selection_softmax(np.zeros(0)).size == 0
+
+
+# ---------------------------------------------------------------- sparse attention
+
+def _mla_case(rng, T, H, dk=40, dv=32, scale=3.0):
+    q = rng.standard_normal((T, H, dk)) * scale
+    kv = rng.standard_normal((T, dk))
+    return q, kv, dv
+
+
+def test_sparse_attention_full_selection_is_causal_sdpa():
+    # every causal key selected: dense causal attention, here torch's scaled_dot_product_attention
+    # (float64, CPU) with the shared entry expanded to every head and the value its first dv
+    # elements; two packed documents through a block-diagonal causal mask
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(21)
+    docs = [13, 7]
+    T, H = sum(docs), 4
+    q, kv, dv = _mla_case(rng, T, H)
+    cu = np.concatenate([[0], np.cumsum(docs)])
+    K = max(docs)
+    idx = np.full((T, K), -1, np.int64)
+    allowed = np.zeros((T, T), bool)
+    for b in range(len(docs)):
+        for u in range(docs[b]):
+            t = cu[b] + u
+            idx[t, :u + 1] = np.arange(cu[b], t + 1)[::-1]          # any slot order
+            allowed[t, cu[b]:t + 1] = True
+    sm = 0.3
+    out, lse = orc.sparse_attention(q, kv, idx, sm, dv=dv)
+    qt = torch.from_numpy(q).permute(1, 0, 2)                       # [H, T, dk]
+    kt = torch.from_numpy(kv)[None].expand(H, T, -1)
+    vt = torch.from_numpy(kv[:, :dv])[None].expand(H, T, -1)
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(allowed), scale=sm)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_sparse_attention_single_and_identical_entries():
+    rng = np.random.default_rng(22)
+    q, kv, dv = _mla_case(rng, 6, 3)
+    sm = 0.7
+    for t in range(6):
+        j = (3 * t + 1) % 6
+        idx = np.full((6, 5), -1)
+        idx[t, 2] = j                                                 # one entry, any slot
+        out, lse = orc.sparse_attention(q, kv, idx, sm, dv=dv)
+        assert np.array_equal(out[t], np.broadcast_to(kv[j, :dv], (3, dv)))    # weight exactly 1
+        np.testing.assert_allclose(lse[t], sm * (q[t] @ kv[j]), rtol=1e-14)
+    # n equal entries: the value itself, log-sum-exp raised by log n
+    kv2 = np.tile(kv[:1], (6, 1))
+    idx = np.tile(np.arange(6), (6, 1))
+    out, lse = orc.sparse_attention(q, kv2, idx, sm, dv=dv)
+    np.testing.assert_allclose(out, np.broadcast_to(kv[0, :dv], out.shape), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse, sm * (q @ kv[0]) + np.log(6.0), rtol=1e-13)
+
+
+def test_sparse_attention_two_entries_are_logistic():
+    rng = np.random.default_rng(23)
+    q, kv, dv = _mla_case(rng, 4, 2, scale=0.5)
+    idx = np.tile([1, 3], (4, 1))
+    out, _ = orc.sparse_attention(q, kv, idx, 1.0, dv=dv)
+    for t in range(4):
+        for h in range(2):
+            d = q[t, h] @ kv[1] - q[t, h] @ kv[3]
+            w = 0.5 * (1.0 + np.tanh(d / 2.0))                       # logistic function of the difference
+            np.testing.assert_allclose(out[t, h], w * kv[1, :dv] + (1 - w) * kv[3, :dv], rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_attention_slots_padding_lengths():
+    rng = np.random.default_rng(24)
+    T, S = 5, 30
+    q = rng.standard_normal((T, 4, 40))
+    kv = rng.standard_normal((S, 40))
+    idx = np.stack([rng.choice(S, 12, replace=False) for _ in range(T)])
+    out, lse = orc.sparse_attention(q, kv, idx, 0.25, dv=32)
+    # slot order does not matter; empty slots (-1) and out-of-range indices are ignored
+    perm = idx[:, rng.permutation(12)]
+    padded = np.concatenate([perm, np.full((T, 3), -1), np.full((T, 2), S + 4)], axis=1)
+    out2, lse2 = orc.sparse_attention(q, kv, padded[:, rng.permutation(17)], 0.25, dv=32)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+    # supplied lengths cut the slot list
+    lens = np.array([0, 1, 5, 12, 40])
+    out3, lse3 = orc.sparse_attention(q, kv, idx, 0.25, dv=32, lengths=lens)
+    assert np.all(out3[0] == 0.0) and np.all(np.isneginf(lse3[0]))           # nothing selected
+    for t in range(1, T):
+        o, l = orc.sparse_attention(q[t:t + 1], kv, idx[t:t + 1, :min(lens[t], 12)], 0.25, dv=32)
+        np.testing.assert_allclose(out3[t], o[0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse3[t], l[0], rtol=1e-13)
+    # a slot listed twice counts twice: like one entry whose score is raised by log 2
+    dup = np.concatenate([idx[:, :1], idx[:, :4]], axis=1)
+    o_dup, l_dup = orc.sparse_attention(q, kv, dup, 0.25, dv=32)
+    s = 0.25 * np.einsum("thd,tjd->thj", q, kv[idx[:, :4]])
+    s[:, :, 0] += np.log(2.0)
+    e = np.exp(s - s.max(axis=2, keepdims=True))
+    w = e / e.sum(axis=2, keepdims=True)
+    np.testing.assert_allclose(o_dup, np.einsum("thj,tjc->thc", w, kv[idx[:, :4], :32]), rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_attention_splits_merge():
+    # attention over a union of two disjoint selections is the log-sum-exp weighted merge of
+    # the two partial attentions (the identity split-KV kernels rely on)
+    rng = np.random.default_rng(25)
+    T, S = 6, 50
+    q = rng.standard_normal((T, 3, 40)) * 2
+    kv = rng.standard_normal((S, 40))
+    idx = np.stack([rng.choice(S, 20, replace=False) for _ in range(T)])
+    o, l = orc.sparse_attention(q, kv, idx, 0.5, dv=32)
+    oa, la = orc.sparse_attention(q, kv, idx[:, :7], 0.5, dv=32)
+    ob, lb = orc.sparse_attention(q, kv, idx[:, 7:], 0.5, dv=32)
+    lm = np.logaddexp(la, lb)
+    np.testing.assert_allclose(l, lm, rtol=1e-13)
+    merged = np.exp(la - lm)[..., None] * oa + np.exp(lb - lm)[..., None] * ob
+    np.testing.assert_allclose(o, merged, rtol=1e-11, atol=1e-12)
