@@ -315,6 +315,40 @@ dsa_status_t dsa_index_forward(
 dsa_status_t dsa_index_selection_softmax(const float* scores, int32_t T, int32_t topk, float* out,
                                          hipStream_t stream);
 
+/*
+ * dsa_index_sparse_attention - absorbed-MLA attention of every query head over the latent
+ * entries its row selected: the consumer of the indexer's top-k (Megatron-LM PR 8403,
+ * "Fused Path": FlashMLA sparse attention after the indexer, compressed KV width 576 =
+ * kv_lora_rank 512 + 64; codex review finding 1: value width 512, invalid slots and
+ * supplied lengths). One latent entry per token serves every head; the key is the whole
+ * entry, the value its first dv elements. For query t the selected entries are the slots
+ * j < lengths[t] (all topk slots when lengths is NULL) whose index lies in [0, S); -1 marks an
+ * empty slot. With s_j = sm_scale * q[t,h,:] . kv[j,:]:
+ *     out[t,h,:]   = sum_j exp(s_j - m) kv[j, 0..dv) / sum_j exp(s_j - m),  m = max_j s_j
+ *     out_lse[t,h] = m + log(sum_j exp(s_j - m))   (natural log)
+ * A row with nothing selected gives zeros and out_lse -inf. A slot listed twice counts twice.
+ *   q        [T, H, dk] bf16, DEVICE, 16-byte aligned.
+ *   kv       [S, dk] bf16, DEVICE, 16-byte aligned (may be NULL when S == 0).
+ *   indices  [T, topk] int32, DEVICE: token indices into kv (the out_indices of a top-k call,
+ *            which hold document offsets already; KPool rows hold expanded token indices).
+ *   lengths  [T] int32, DEVICE, or NULL: slots used per row (out_lengths of a top-k call),
+ *            clamped to [0, topk].
+ *   dk, dv   576 and 512 (DSA_ERR_UNSUPPORTED otherwise); H a multiple of 16.
+ *   out      [T, H, dv] bf16, DEVICE, 16-byte aligned, caller-owned.
+ *   out_lse  [T, H] fp32, DEVICE, or NULL (not written).
+ * Arithmetic: q.k products in fp32 on MFMA (bf16 operands); softmax in fp32, base 2, with the
+ * weights rounded to bf16 (nearest even) for the value product and summed in fp32 for the
+ * normaliser; output rounded to bf16 (nearest even). Results do not depend on scheduling.
+ * Errors: DSA_ERR_INVALID_ARGUMENT for T < 0, S < 0, H < 1, topk < 1, a non-finite sm_scale,
+ * NULL or misaligned pointers (T > 0); DSA_ERR_UNSUPPORTED for other widths, H % 16 != 0 or
+ * S * dk * 2 >= 2^31; DSA_ERR_DEVICE if the launch fails. Index values are not an error:
+ * anything outside [0, S) is an empty slot.
+ */
+dsa_status_t dsa_index_sparse_attention(const void* q, const void* kv, const int32_t* indices,
+                                        const int32_t* lengths, int32_t T, int32_t H, int32_t S, int32_t topk,
+                                        int32_t dk, int32_t dv, float sm_scale, void* out, float* out_lse,
+                                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "score_fused", "topk", "forward",
-           "forward_workspace_size", "selection_softmax", "library_path", "load", "PRECISIONS", "DsaError"]
+           "forward_workspace_size", "selection_softmax", "sparse_attention", "library_path", "load", "PRECISIONS", "DsaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libdsa_index.so"
@@ -77,6 +77,8 @@ def load():
                                       i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dsa_index_selection_softmax.restype = i32
     lib.dsa_index_selection_softmax.argtypes = [vp, i32, i32, vp, vp]
+    lib.dsa_index_sparse_attention.restype = i32
+    lib.dsa_index_sparse_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]
     lib.dsa_index_score_fused.restype = i32
     lib.dsa_index_score_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32,
                                           i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
@@ -402,3 +404,39 @@ def selection_softmax(scores, *, out=None):
     _check(st, "dsa_index_selection_softmax")
     return out
 
+
+def sparse_attention(q, kv, indices, *, sm_scale, lengths=None, out=None, lse=None, return_lse=True):
+    """Absorbed-MLA attention over the selected latent entries.
+
+    q [T, H, 576] bf16, kv [S, 576] bf16, indices [T, topk] int32 (token indices, -1 empty),
+    lengths [T] int32 or None. Returns out [T, H, 512] bf16 and, with ``return_lse``, the
+    natural-log log-sum-exp [T, H] fp32."""
+    lib = load()
+    _need(q, "q", (torch.bfloat16,))
+    _need(kv, "kv", (torch.bfloat16,), device=q.device)
+    _need(indices, "indices", (torch.int32,), device=q.device)
+    _need(lengths, "lengths", (torch.int32,), device=q.device)
+    if q.dim() != 3 or kv.dim() != 2 or indices.dim() != 2:
+        raise ValueError("q must be [T, H, dk], kv [S, dk] and indices [T, topk]")
+    T, H, dk = q.shape
+    S, dk2 = kv.shape
+    if dk2 != dk or indices.shape[0] != T:
+        raise ValueError(f"shapes do not agree: q {tuple(q.shape)}, kv {tuple(kv.shape)}, indices {tuple(indices.shape)}")
+    if lengths is not None and tuple(lengths.shape) != (T,):
+        raise ValueError(f"lengths must be [T], got {tuple(lengths.shape)}")
+    dv = 512
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", (torch.bfloat16,), device=q.device)
+    if tuple(out.shape) != (T, H, dv):
+        raise ValueError(f"out must be [{T}, {H}, {dv}], got {tuple(out.shape)}")
+    if return_lse and lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", (torch.float32,), device=q.device)
+    if lse is not None and tuple(lse.shape) != (T, H):
+        raise ValueError(f"lse must be [{T}, {H}], got {tuple(lse.shape)}")
+    st = lib.dsa_index_sparse_attention(_ptr(q), _ptr(kv), _ptr(indices), _ptr(lengths), int(T), int(H), int(S),
+                                        int(indices.shape[1]), int(dk), int(dv), float(sm_scale), _ptr(out),
+                                        _ptr(lse), _stream(q.device))
+    _check(st, "dsa_index_sparse_attention")
+    return (out, lse) if return_lse else out

@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or synchronises the host.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -467,6 +468,32 @@ dsa_status_t dsa_index_selection_softmax(const float* scores, int32_t T, int32_t
   if (!aligned(scores, 4) || !aligned(out, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "scores and out must be 4-byte aligned");
   hipError_t e = dsa::launch_selection_softmax(scores, T, topk, out, stream);
   if (e != hipSuccess) return device_fail(e, "dsa_index_selection_softmax");
+  return DSA_OK;
+}
+
+dsa_status_t dsa_index_sparse_attention(const void* q, const void* kv, const int32_t* indices,
+                                        const int32_t* lengths, int32_t T, int32_t H, int32_t S, int32_t topk,
+                                        int32_t dk, int32_t dv, float sm_scale, void* out, float* out_lse,
+                                        hipStream_t stream) {
+  if (T < 0 || S < 0 || H < 1 || topk < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "need T >= 0, S >= 0, H >= 1 and topk >= 1 (T=%d, S=%d, H=%d, topk=%d)", T,
+                S, H, topk);
+  if (dk != dsa::kMlaKeyWidth || dv != dsa::kMlaValueWidth)
+    return fail(DSA_ERR_UNSUPPORTED, "entry width %d / value width %d: only %d / %d is supported", dk, dv,
+                dsa::kMlaKeyWidth, dsa::kMlaValueWidth);
+  if (H % 16 != 0) return fail(DSA_ERR_UNSUPPORTED, "H must be a multiple of 16 (H=%d)", H);
+  if ((long long)S * dk * 2 > 0x7FFFFFFFll)
+    return fail(DSA_ERR_UNSUPPORTED, "the latent tensor must stay below 2 GiB (S=%d)", S);
+  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (T == 0) return DSA_OK;
+  if (!q || !indices || !out || (S > 0 && !kv))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q, indices, out (and kv when S > 0) must not be NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(indices, 4) ||
+      (lengths && !aligned(lengths, 4)) || (out_lse && !aligned(out_lse, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q, kv, out must be 16-byte aligned; indices, lengths, out_lse 4-byte");
+  hipError_t e = dsa::launch_sparse_mla(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), indices,
+                                        lengths, T, H, S, topk, sm_scale, static_cast<uint16_t*>(out), out_lse, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_sparse_attention");
   return DSA_OK;
 }
 

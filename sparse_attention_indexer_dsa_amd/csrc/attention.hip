@@ -1,0 +1,284 @@
+// Sparse absorbed-MLA attention over the indexer's selection (gfx950).
+//
+// The consumer of the top-k: every query head attends only to the latent entries its row
+// selected (Megatron-LM PR 8403, "Fused Path": FlashMLA sparse attention after the indexer,
+// compressed KV width 576 = kv_lora_rank 512 + 64; codex review finding 1: value width 512,
+// invalid slots and supplied lengths). One 576-wide bf16 entry per token serves every head:
+// the key is the whole entry, the value its first 512 elements. For query t, head h and the
+// selected entries j (slots j < length[t] holding a valid token index):
+//     out[t,h,:] = sum_j softmax_j(sm_scale * q[t,h,:] . kv[j,:]) kv[j,:512]
+//     lse[t,h]   = log sum_j exp(sm_scale * q[t,h,:] . kv[j,:])
+//
+// Work decomposition. A workgroup of 4 waves owns one query token and 64 of its heads, one
+// wave per 16 heads; the wave's q operands (16 heads x 576) stay in registers. The row's
+// slots are swept in tiles of 32: the workgroup gathers the 32 selected entries into LDS
+// twice, key-major for the scores (contraction over the 576 elements) and as groups of 8
+// keys per value element for the weighted sum (contraction over keys), so both products
+// read their MFMA operands as 16-byte LDS loads. Entries are read through a buffer
+// descriptor over the latent tensor: an empty slot or an index outside [0, S) reads zeros
+// without touching memory and its score is masked.
+//
+// Softmax: online, in base 2 (scores pre-multiplied by sm_scale * log2 e). The running row
+// maximum is raised only when a tile's maximum exceeds it by more than 8 (then the 128
+// accumulator registers are rescaled); otherwise weights up to 2^8 accumulate against the
+// older maximum, which is exact in real arithmetic and keeps the rescale off the common
+// path. Weights enter the value product as bf16 (nearest even); the normaliser sums them in
+// fp32. Workgroups are numbered so that each XCD (block b runs on XCD b % 8) takes a
+// contiguous range of tokens, whose selections overlap, through its own L2.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 (lane l): A holds row l%16, 8 consecutive k from 8(l/16);
+// B holds column l%16, the same k; the 16x16 fp32 result gives lane l column l%16, rows
+// 4(l/16) .. 4(l/16)+3.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDK = kMlaKeyWidth, kDV = kMlaValueWidth;
+constexpr int kRowB = kDK * 2;                 // bytes per latent entry
+constexpr int kNK = 32;                        // slots per tile
+constexpr int kKPitch = kRowB + 16;            // key-major LDS row (16-byte skew between keys)
+constexpr int kPPitch = (kNK + 8) * 2;         // weight staging row (one head, 32 keys)
+constexpr int kLdsK = kNK * kKPitch;
+constexpr int kLdsV = (kNK / 8) * kDV * 16;    // [key group][value element][8 keys]
+constexpr int kLdsP = 4 * 16 * kPPitch;
+constexpr int kLdsBytes = kLdsK + kLdsV + kLdsP;
+constexpr int kSteps = kDK / 32;               // MFMA k-steps of the score product
+constexpr int kVBlocks = kDV / 16;             // 16-column blocks of the value product
+static_assert(kDK % 32 == 0 && kDV % 128 == 0 && kDV < kDK, "entry layout");
+static_assert(4 * 16 * kDV * 2 <= kLdsBytes, "the output staging reuses the tile buffers");
+
+struct AttnArgs {
+  const uint16_t* q; const uint16_t* kv; const int32_t* indices; const int32_t* lengths;
+  int T, H, S, topk;
+  float scale_log2;      // sm_scale * log2(e)
+  int tper;              // tokens per XCD range
+  uint16_t* out; float* lse;
+};
+
+// Max / sum over the 16 lanes of a DPP row (row rotations; every lane gets the result).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
+  return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
+__global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* kt = smem;                          // [32 keys][kKPitch]
+  uint8_t* vt = smem + kLdsK;                  // [4][kDV][8 keys] bf16
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* pst = smem + kLdsK + kLdsV + wv * 16 * kPPitch;   // this wave's weights [16 heads][32 keys]
+
+  const int nhb = (a.H + 63) / 64;
+  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
+  const int t = xcd * a.tper + seq / nhb;
+  if (t >= a.T) return;                        // whole workgroup
+  const int h0 = (seq % nhb) * 64 + 16 * wv;
+  const bool active = h0 < a.H;                // wave-uniform: a wave past the heads only gathers
+  const int n = a.lengths ? clampi(__ldg(a.lengths + t), 0, a.topk) : a.topk;
+  const int32_t* irow = a.indices + (long long)t * a.topk;
+  const int kvbytes = a.S * kRowB;             // the descriptor's end; offsets there read zeros
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(a.kv, kvbytes);
+  auto entry_off = [&](int j) {                // byte offset of slot j's entry, or past the end
+    const int ix = j < n ? __ldg(irow + j) : -1;
+    return (ix >= 0 && ix < a.S) ? ix * kRowB : kvbytes;
+  };
+
+  const int r16 = lane & 15, g4 = lane >> 4;
+  // q operands: head h0 + r16, elements 32*ks + 8*g4 .. +7
+  bf16x8 qa[kSteps];
+  if (active) {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((long long)t * a.H + h0 + r16) * kDK + 8 * g4);
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const uint4 v = qp[4 * ks];
+      qa[ks] = *reinterpret_cast<const bf16x8*>(&v);
+    }
+  }
+  f32x4 o[kVBlocks];
+#pragma unroll
+  for (int c = 0; c < kVBlocks; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], lsum[4];                         // rows 4*g4 + i: running maximum, lane's weight sum
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; lsum[i] = 0.f; }
+
+  for (int j0 = 0; j0 < n; j0 += kNK) {
+    __syncthreads();                           // the previous tile is no longer read
+    // ---- gather. Value part: wave wv takes keys 8wv .. 8wv+7 (slot indices uniform, read on
+    //      the scalar unit), lane l their 16 bytes of elements 8l .. 8l+7; the key-major copy
+    //      is written as loaded and the 8 x 8 block is transposed in registers into the
+    //      grouped layout. The last 64 elements: thread tid takes key tid/8, 16-byte piece tid%8.
+    {
+      // two halves of 4 keys (fewer registers in flight next to the resident operands)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int off = entry_off(j0 + 8 * wv + 4 * hf + k);
+          raw[k] = __builtin_amdgcn_raw_buffer_load_b128(rkv, off == kvbytes ? off : off + 16 * lane, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<u32x4*>(kt + (8 * wv + 4 * hf + k) * kKPitch + 16 * lane) = raw[k];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          // element 8*lane + d of the 4 keys: half d%2 of word d/2 of each key's piece
+          uint2 w;
+          const uint32_t a0 = raw[0][d >> 1], a1 = raw[1][d >> 1], a2 = raw[2][d >> 1], a3 = raw[3][d >> 1];
+          w.x = (d & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+          w.y = (d & 1) ? ((a2 >> 16) | (a3 & 0xFFFF0000u)) : ((a2 & 0xFFFFu) | (a3 << 16));
+          *reinterpret_cast<uint2*>(vt + (wv * kDV + 8 * lane + d) * 16 + 8 * hf) = w;
+        }
+      }
+      const int kr = tid >> 3, pc = tid & 7;
+      const int offr = entry_off(j0 + kr);
+      const u32x4 rope = __builtin_amdgcn_raw_buffer_load_b128(rkv, offr == kvbytes ? offr : offr + 2 * kDV + 16 * pc, 0, 0);
+      *reinterpret_cast<u32x4*>(kt + kr * kKPitch + 2 * kDV + 16 * pc) = rope;
+    }
+    // slots of this tile that hold an entry (bit j - j0)
+    uint32_t vmask;
+    {
+      const int j = j0 + (lane & 31);
+      const int ix = j < n ? __ldg(irow + j) : -1;
+      vmask = (uint32_t)__ballot(lane < 32 && ix >= 0 && ix < a.S);
+    }
+    __syncthreads();
+    if (!active) continue;
+
+    // ---- scores of 16 heads x 32 keys: lane holds keys r16 (s0) and 16 + r16 (s1), rows 4*g4 + i
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(kt + r16 * kKPitch + 64 * ks + 16 * g4);
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(kt + (16 + r16) * kKPitch + 64 * ks + 16 * g4);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b0), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b1), s1, 0, 0, 0);
+    }
+    const bool v0 = (vmask >> r16) & 1u, v1 = (vmask >> (16 + r16)) & 1u;
+    float x0[4], x1[4], mt[4];
+    bool raise = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x0[i] = v0 ? s0[i] * a.scale_log2 : -INFINITY;
+      x1[i] = v1 ? s1[i] * a.scale_log2 : -INFINITY;
+      mt[i] = row16_max(fmaxf(x0[i], x1[i]));
+      raise |= mt[i] > m[i] + 8.f;
+    }
+    if (__ballot(raise) != 0ull) {
+      // new maxima (every row of the wave, so the decision stays uniform)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mn = fmaxf(m[i], mt[i]);
+        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[i] - mn);   // exp2(-inf) = 0 at the start
+        m[i] = mn;
+        lsum[i] *= alpha;
+#pragma unroll
+        for (int c = 0; c < kVBlocks; ++c) o[c][i] *= alpha;
+      }
+    }
+    // weights (valid slots have finite scores and a finite maximum); bf16 to the staging rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = v0 ? exp2f(x0[i] - m[i]) : 0.f;
+      const float p1 = v1 ? exp2f(x1[i] - m[i]) : 0.f;
+      lsum[i] += p0 + p1;
+      uint16_t* prow = reinterpret_cast<uint16_t*>(pst + (4 * g4 + i) * kPPitch);
+      prow[r16] = f32_to_bf16_rne(p0);
+      prow[16 + r16] = f32_to_bf16_rne(p1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- weighted values: A = weights (head r16, keys 8*g4 .. +7), B = values (column
+    //      16c + r16, the same keys)
+    const u32x4 pv = *reinterpret_cast<const u32x4*>(pst + r16 * kPPitch + 16 * g4);
+    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pv);
+#pragma unroll
+    for (int c = 0; c < kVBlocks; ++c) {
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(vt + (g4 * kDV + 16 * c + r16) * 16);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, *reinterpret_cast<const bf16x8*>(&bv), o[c], 0, 0, 0);
+    }
+  }
+
+  // ---- normalise, stage the wave's 16 x 512 bf16 rows in LDS, store them contiguously
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float l = row16_sum(lsum[i]);
+    inv[i] = l > 0.f ? 1.f / l : 0.f;
+    if (a.lse && active && r16 == 0)
+      a.lse[(long long)t * a.H + h0 + 4 * g4 + i] = l > 0.f ? (m[i] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+  }
+  __syncthreads();                             // every wave is done with the tile buffers
+  if (!active) return;
+  uint8_t* ost = smem + wv * 16 * kDV * 2;
+#pragma unroll
+  for (int c = 0; c < kVBlocks; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<uint16_t*>(ost + (4 * g4 + i) * kDV * 2)[16 * c + r16] = f32_to_bf16_rne(o[c][i] * inv[i]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint4* dst = reinterpret_cast<uint4*>(a.out + ((long long)t * a.H + h0) * kDV);
+#pragma unroll
+  for (int r = 0; r < 16 * kDV * 2 / 16 / 64; ++r)
+    dst[r * 64 + lane] = reinterpret_cast<const uint4*>(ost)[r * 64 + lane];
+}
+
+}  // namespace
+
+hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const int32_t* lengths,
+                             int T, int H, int S, int topk, float sm_scale, uint16_t* out, float* lse,
+                             hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  {
+    // more than 64 KB of dynamic LDS: allowed once per device
+    static std::mutex mu;
+    static bool done[64] = {false};
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (device >= 64 || !done[device]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_mla_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      if (e != hipSuccess) return e;
+      if (device < 64) done[device] = true;
+    }
+  }
+  AttnArgs a;
+  a.q = q; a.kv = kv; a.indices = indices; a.lengths = lengths;
+  a.T = T; a.H = H; a.S = S; a.topk = topk;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.tper = (T + 7) / 8;
+  a.out = out; a.lse = lse;
+  const int nhb = (H + 63) / 64;
+  const long long blocks = 8ll * a.tper * nhb;
+  hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -59,6 +59,13 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st);
 
 hipError_t launch_selection_softmax(const float* scores, int T, int topk, float* out, hipStream_t st);
 
+// Sparse absorbed-MLA attention: latent entry width (key) and value width, in elements.
+constexpr int kMlaKeyWidth = 576;
+constexpr int kMlaValueWidth = 512;
+hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const int32_t* lengths,
+                             int T, int H, int S, int topk, float sm_scale, uint16_t* out, float* lse,
+                             hipStream_t st);
+
 // Largest row (candidates) the LDS top-k supports.
 constexpr int kTopkMaxCand = 32768;
 

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
     assert {"dsa_index_preprocess", "dsa_index_kpool", "dsa_index_workspace_size", "dsa_index_score_topk",
             "dsa_index_score", "dsa_index_topk", "dsa_index_forward", "dsa_index_forward_workspace_size",
-            "dsa_index_score_fused", "dsa_index_selection_softmax",
+            "dsa_index_score_fused", "dsa_index_selection_softmax", "dsa_index_sparse_attention",
             "dsa_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -174,6 +174,30 @@ def test_selection_softmax_validation(lib):
     assert f(FAKE + 2, 4, 8, FAKE, None) == 1               # misaligned
     assert b"aligned" in lib.dsa_last_error()
     assert f(None, 0, 8, None, None) == 0                   # empty problem: nothing to do
+
+
+def test_sparse_attention_validation(lib):
+    f = lib.dsa_index_sparse_attention
+    ok = dict(q=FAKE, kv=FAKE, idx=FAKE, lens=None, T=4, H=64, S=100, topk=32, dk=576, dv=512, sc=0.1, out=FAKE,
+              lse=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kv"], a["idx"], a["lens"], a["T"], a["H"], a["S"], a["topk"], a["dk"], a["dv"], a["sc"],
+                 a["out"], a["lse"], None)
+
+    assert call(T=-1) == 1 and call(S=-1) == 1 and call(H=0) == 1 and call(topk=0) == 1
+    assert call(sc=float("inf")) == 1 and call(sc=float("nan")) == 1
+    assert call(dk=512) == 2 and call(dv=448) == 2                    # widths other than 576 / 512
+    assert b"576" in lib.dsa_last_error()
+    assert call(H=24) == 2                                             # heads in groups of 16
+    assert call(S=1 << 21) == 2                                        # latent tensor of 2 GiB or more
+    assert call(q=None) == 1 and call(idx=None) == 1 and call(out=None) == 1
+    assert call(kv=None) == 1
+    assert call(q=FAKE + 8) == 1 and call(out=FAKE + 4) == 1 and call(lse=FAKE + 2) == 1
+    assert call(lens=FAKE + 2) == 1
+    assert b"aligned" in lib.dsa_last_error()
+    assert call(T=0, q=None, idx=None, out=None, lse=None, kv=None) == 0   # empty problem: nothing to do
 
 
 def test_python_binding_maps_errors():
