@@ -60,7 +60,7 @@ def pair_count(cu, kp):
     return tot
 
 
-def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False):
+def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False, attn_heads=0):
     import torch
     import sparse_attention_indexer_dsa_amd as dsa
     import parity
@@ -96,6 +96,15 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False):
     ws = torch.empty(dsa.workspace_size(T, max_seqlen, topk, kp, H, D, B, prec), dtype=torch.uint8, device=dev)
     outs = dsa._alloc_outputs(None, T, topk, kp, dev)
     sm_out = torch.empty((T, topk), dtype=torch.float32, device=dev) if softmax else None
+    attn = {}
+    if attn_heads:
+        # sparse attention over the selection: synthetic bf16 queries [T, heads, 576] and one
+        # latent entry [576] per token, drawn on the device
+        gen_t = torch.Generator(device=dev).manual_seed(7)
+        attn["q"] = torch.randn((T, attn_heads, 576), generator=gen_t, device=dev).to(torch.bfloat16)
+        attn["kv"] = torch.randn((T, 576), generator=gen_t, device=dev).to(torch.bfloat16)
+        attn["out"] = torch.empty((T, attn_heads, 512), dtype=torch.bfloat16, device=dev)
+        attn["lse"] = torch.empty((T, attn_heads), dtype=torch.float32, device=dev)
     k_op = pool["pooled_op"] if kp > 1 else (ops["k_op"] if inp["preprocess"] else d["k"])
     k_scale = pool.get("pooled_scale") if kp > 1 else ops.get("k_scale")
 
@@ -133,6 +142,11 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False):
             dsa.selection_softmax(outs["scores"], out=sm_out)
         if ev is not None:
             ev[i].record(); i += 1
+        if attn_heads:
+            dsa.sparse_attention(attn["q"], attn["kv"], outs["indices"], sm_scale=576 ** -0.5,
+                                 lengths=outs["lengths"], out=attn["out"], lse=attn["lse"])
+        if ev is not None:
+            ev[i].record(); i += 1
 
     for _ in range(warmup):
         step()
@@ -158,7 +172,7 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False):
     # Per-kernel durations: the same steps run eagerly with HIP events around every library
     # call on the stream the kernels run on, queued behind a spin kernel so that the stream
     # never waits for the host between a kernel and its events.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     torch.cuda._sleep(20_000_000)
     for s in range(steps):
         step(events[s])
@@ -170,9 +184,11 @@ def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False):
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-    names = ["preprocess", "kpool", "score", "topk", "softmax"]
+    names = ["preprocess", "kpool", "score", "topk", "softmax", "attention"]
     per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])) / 1e3
            for i, n in enumerate(names)}
+    # slots the attention reads per step (the selection's token lengths)
+    per["attention_slots"] = int(outs["lengths"].sum().item()) if attn_heads else 0
     return (t1 - t0), per, fused
 
 
@@ -293,6 +309,9 @@ def main():
     ap.add_argument("--softmax", action="store_true",
                     help="also compute the softmax over each row's selection (dsa_index_selection_softmax) in "
                          "every step")
+    ap.add_argument("--attention", type=int, default=0, metavar="HEADS",
+                    help="also run the sparse MLA attention over each row's selection "
+                         "(dsa_index_sparse_attention) with this many query heads in every step")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="record scoring-kernel traffic from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
@@ -311,7 +330,8 @@ def main():
     kp = inp["kpool"]
     pairs = pair_count(inp["cu_seqlens"], kp)
     print(f"[bench] workload {args.workload}: {inp['name']} T={T} pairs={pairs}", file=sys.stderr, flush=True)
-    elapsed, per, fused = run_gpu(inp, args.steps, args.warmup, args.copy_mb, args.fuse, args.softmax)
+    elapsed, per, fused = run_gpu(inp, args.steps, args.warmup, args.copy_mb, args.fuse, args.softmax,
+                                  args.attention)
     alg = algorithmic(inp, pairs, fused)
     prec = inp["precision"]
     kernels = {}
@@ -328,6 +348,12 @@ def main():
             k["gbps"] = round(b / per[n] / 1e9, 1)
             k["frac_hbm"] = round(b / per[n] / PEAK_HBM, 4)
         kernels[n] = k
+    if args.attention and per["attention"] > 0:
+        # score and value products over every selected slot: 2 * heads * (576 + 512) flops each
+        fl = 2.0 * per["attention_slots"] * args.attention * (576 + 512)
+        kernels["attention"] = {"ms": round(per["attention"] * 1e3, 4), "tflops": round(fl / per["attention"] / 1e12, 1),
+                                "frac_mfma": round(fl / per["attention"] / PEAK_FLOPS["bf16"], 4),
+                                "heads": args.attention, "slots": per["attention_slots"]}
     achieved = alg["score_flops"] / per["score"] / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -351,7 +377,7 @@ def main():
                    else f"{len(inp['docs'])} docs", "topk": inp["topk"], "kpool": kp, "precision": prec,
                    "preprocess": bool(inp["preprocess"]), "query_preprocessing": "in the scoring kernel" if fused
                    else ("own kernel" if inp["preprocess"] else "none"), "pairs_per_step": pairs,
-                   "selection_softmax": bool(args.softmax),
+                   "selection_softmax": bool(args.softmax), "sparse_attention_heads": args.attention,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "score", "achieved": round(achieved, 2),
                      "peak": PEAK_FLOPS[prec] / 1e12, "unit": "TFLOP/s",

@@ -49,7 +49,11 @@ constexpr int kNK = 32;                        // slots per tile
 constexpr int kKPitch = kRowB + 16;            // key-major LDS row (16-byte skew between keys)
 constexpr int kPPitch = (kNK + 8) * 2;         // weight staging row (one head, 32 keys)
 constexpr int kLdsK = kNK * kKPitch;
-constexpr int kLdsV = (kNK / 8) * kDV * 16;    // [key group][value element][8 keys]
+// [key group][value element][8 keys], element c of a group in 16-byte slot c + c/8: a lane's
+// writes (8 consecutive elements per lane) then fall 9 slots apart and the operand reads (16
+// consecutive elements) nearly so, both spread over the banks
+constexpr int kVSlots = kDV + kDV / 8;
+constexpr int kLdsV = (kNK / 8) * kVSlots * 16;
 constexpr int kLdsP = 4 * 16 * kPPitch;
 constexpr int kLdsBytes = kLdsK + kLdsV + kLdsP;
 constexpr int kSteps = kDK / 32;               // MFMA k-steps of the score product
@@ -64,6 +68,9 @@ struct AttnArgs {
   int tper;              // tokens per XCD range
   uint16_t* out; float* lse;
 };
+
+// bf16 bits of x, nearest even (one v_cvt_pk_bf16_f32 on gfx950; the values here are finite).
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // Max / sum over the 16 lanes of a DPP row (row rotations; every lane gets the result).
 __device__ __forceinline__ float row16_max(float x) {
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
           const uint32_t a0 = raw[0][d >> 1], a1 = raw[1][d >> 1], a2 = raw[2][d >> 1], a3 = raw[3][d >> 1];
           w.x = (d & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
           w.y = (d & 1) ? ((a2 >> 16) | (a3 & 0xFFFF0000u)) : ((a2 & 0xFFFFu) | (a3 << 16));
-          *reinterpret_cast<uint2*>(vt + (wv * kDV + 8 * lane + d) * 16 + 8 * hf) = w;
+          *reinterpret_cast<uint2*>(vt + (wv * kVSlots + 9 * lane + d) * 16 + 8 * hf) = w;
         }
       }
       const int kr = tid >> 3, pc = tid & 7;
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float mn = fmaxf(m[i], mt[i]);
-        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[i] - mn);   // exp2(-inf) = 0 at the start
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);   // exp2(-inf) = 0 at the start
         m[i] = mn;
         lsum[i] *= alpha;
 #pragma unroll
@@ -201,12 +208,12 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
     // weights (valid slots have finite scores and a finite maximum); bf16 to the staging rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p0 = v0 ? exp2f(x0[i] - m[i]) : 0.f;
-      const float p1 = v1 ? exp2f(x1[i] - m[i]) : 0.f;
+      const float p0 = v0 ? __builtin_amdgcn_exp2f(x0[i] - m[i]) : 0.f;
+      const float p1 = v1 ? __builtin_amdgcn_exp2f(x1[i] - m[i]) : 0.f;
       lsum[i] += p0 + p1;
       uint16_t* prow = reinterpret_cast<uint16_t*>(pst + (4 * g4 + i) * kPPitch);
-      prow[r16] = f32_to_bf16_rne(p0);
-      prow[16 + r16] = f32_to_bf16_rne(p1);
+      prow[r16] = bf16_bits(p0);
+      prow[16 + r16] = bf16_bits(p1);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
     const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pv);
 #pragma unroll
     for (int c = 0; c < kVBlocks; ++c) {
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(vt + (g4 * kDV + 16 * c + r16) * 16);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(vt + (g4 * kVSlots + 18 * c + r16 + (r16 >> 3)) * 16);
       o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, *reinterpret_cast<const bf16x8*>(&bv), o[c], 0, 0, 0);
     }
   }
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
   for (int c = 0; c < kVBlocks; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      reinterpret_cast<uint16_t*>(ost + (4 * g4 + i) * kDV * 2)[16 * c + r16] = f32_to_bf16_rne(o[c][i] * inv[i]);
+      reinterpret_cast<uint16_t*>(ost + (4 * g4 + i) * kDV * 2)[16 * c + r16] = bf16_bits(o[c][i] * inv[i]);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
