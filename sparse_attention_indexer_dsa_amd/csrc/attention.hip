@@ -107,10 +107,6 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
   const int32_t* irow = a.indices + (long long)t * a.topk;
   const int kvbytes = a.S * kRowB;             // the descriptor's end; offsets there read zeros
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(a.kv, kvbytes);
-  auto entry_off = [&](int j) {                // byte offset of slot j's entry, or past the end
-    const int ix = j < n ? __ldg(irow + j) : -1;
-    return (ix >= 0 && ix < a.S) ? ix * kRowB : kvbytes;
-  };
 
   const int r16 = lane & 15, g4 = lane >> 4;
   // q operands: head h0 + r16, elements 32*ks + 8*g4 .. +7
@@ -130,21 +126,56 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; lsum[i] = 0.f; }
 
+  // Slot indices are read a tile ahead: the 8 value-part keys of this wave (uniform, scalar
+  // registers), the key of this thread's last-64-element piece and the slot of mask lane l%32.
+  const int kr = tid >> 3, pc = tid & 7;
+  int ixv[8], ixr = -1, ixm = -1;
+  // Every load is issued (addresses clamped into the row, slots past n replaced by -1), so
+  // that the wait counts stay exact on every path.
+  auto load_indices = [&](int j0) {
+    const int last = a.topk - 1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + 8 * wv + k;
+      const int v = __ldg(irow + min(j, last));
+      ixv[k] = j < n ? v : -1;
+    }
+    const int vr = __ldg(irow + min(j0 + kr, last));
+    ixr = j0 + kr < n ? vr : -1;
+    const int jm = j0 + (lane & 31);
+    const int vm = __ldg(irow + min(jm, last));
+    ixm = jm < n ? vm : -1;
+  };
+  auto off_of = [&](int ix) { return (ix >= 0 && ix < a.S) ? ix * kRowB : kvbytes; };
+  if (n > 0) load_indices(0);
+
   for (int j0 = 0; j0 < n; j0 += kNK) {
     __syncthreads();                           // the previous tile is no longer read
-    // ---- gather. Value part: wave wv takes keys 8wv .. 8wv+7 (slot indices uniform, read on
-    //      the scalar unit), lane l their 16 bytes of elements 8l .. 8l+7; the key-major copy
-    //      is written as loaded and the 8 x 8 block is transposed in registers into the
-    //      grouped layout. The last 64 elements: thread tid takes key tid/8, 16-byte piece tid%8.
+    // ---- gather. Value part: wave wv takes keys 8wv .. 8wv+7, lane l their 16 bytes of
+    //      elements 8l .. 8l+7, in two halves of 4 keys (fewer registers next to the resident
+    //      operands); the key-major copy is written as loaded and each 4 x 8 block is
+    //      transposed in registers into the grouped layout. The last 64 elements: thread tid
+    //      takes key tid/8, piece tid%8, loaded together with the first half.
+    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && ixm >= 0 && ixm < a.S);   // valid slots (bit j - j0)
     {
-      // two halves of 4 keys (fewer registers in flight next to the resident operands)
+      int cv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cv[k] = ixv[k];
+      const int offr = off_of(ixr);
+      const u32x4 rope = __builtin_amdgcn_raw_buffer_load_b128(rkv, offr == kvbytes ? offr : offr + 2 * kDV + 16 * pc, 0, 0);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         u32x4 raw[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int off = entry_off(j0 + 8 * wv + 4 * hf + k);
+          const int off = off_of(cv[4 * hf + k]);
           raw[k] = __builtin_amdgcn_raw_buffer_load_b128(rkv, off == kvbytes ? off : off + 16 * lane, 0, 0);
+        }
+        if (hf == 0) {
+          // the next tile's indices, in flight during this tile (loads complete in order, so
+          // they are issued after the first gathers)
+          load_indices(j0 + kNK);              // past the row: clamped reads, unused
+          *reinterpret_cast<u32x4*>(kt + kr * kKPitch + 2 * kDV + 16 * pc) = rope;
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -159,17 +190,6 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
           *reinterpret_cast<uint2*>(vt + (wv * kVSlots + 9 * lane + d) * 16 + 8 * hf) = w;
         }
       }
-      const int kr = tid >> 3, pc = tid & 7;
-      const int offr = entry_off(j0 + kr);
-      const u32x4 rope = __builtin_amdgcn_raw_buffer_load_b128(rkv, offr == kvbytes ? offr : offr + 2 * kDV + 16 * pc, 0, 0);
-      *reinterpret_cast<u32x4*>(kt + kr * kKPitch + 2 * kDV + 16 * pc) = rope;
-    }
-    // slots of this tile that hold an entry (bit j - j0)
-    uint32_t vmask;
-    {
-      const int j = j0 + (lane & 31);
-      const int ix = j < n ? __ldg(irow + j) : -1;
-      vmask = (uint32_t)__ballot(lane < 32 && ix >= 0 && ix < a.S);
     }
     __syncthreads();
     if (!active) continue;
