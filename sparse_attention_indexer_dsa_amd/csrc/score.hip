@@ -374,13 +374,24 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      // unconditional loads (rows past the document read its last token and are zeroed
+      // below) under one uniform dtype branch, so the 16 loads are in flight together
       const int rr = rb * 32 + (i / 4) * 8 + hl * 4 + (i % 4);
-      const int tl2 = rr / H, h2 = rr % H;
-      float wv_ = 0.f;
-      if (ut0 + tl2 < L) {
-        const long long wi = (long long)(lo + ut0 + tl2) * H + h2;
-        wv_ = a.w_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.w)[wi]) : reinterpret_cast<const float*>(a.w)[wi];
+      const long long wi = (long long)(lo + min(ut0 + rr / H, L - 1)) * H + rr % H;
+      wl[rb][i] = a.w_bf16 ? 0.f : reinterpret_cast<const float*>(a.w)[wi];
+    }
+    if (a.w_bf16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = rb * 32 + (i / 4) * 8 + hl * 4 + (i % 4);
+        const long long wi = (long long)(lo + min(ut0 + rr / H, L - 1)) * H + rr % H;
+        wl[rb][i] = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.w)[wi]);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = rb * 32 + (i / 4) * 8 + hl * 4 + (i % 4);
+      const float wv_ = ut0 + rr / H < L ? wl[rb][i] : 0.f;
       wl[rb][i] = wv_;
       if (kWLds && col < 4 && (i % 4) == col) w_lds[wv * 64 + rr] = wv_;   // each row once
     }
