@@ -95,6 +95,38 @@ __device__ __forceinline__ void load_in(const void* base, long long off, float (
   }
 }
 
+// The same loads as load_in, kept as raw words (converted later by convert_in), so that
+// loads issued before a branch stay in flight across it.
+template <bool IN_BF16, int N>
+using RawIn = uint4[IN_BF16 ? N / 8 : N / 4];
+
+template <bool IN_BF16, int N>
+__device__ __forceinline__ void load_raw(const void* base, long long off, RawIn<IN_BF16, N>& r) {
+  constexpr int NR = IN_BF16 ? N / 8 : N / 4;
+#pragma unroll
+  for (int c = 0; c < NR; ++c)
+    r[c] = IN_BF16 ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off + 8 * c)
+                   : *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + off + 4 * c);
+}
+
+template <bool IN_BF16, int N>
+__device__ __forceinline__ void convert_in(const RawIn<IN_BF16, N>& r, float (&x)[N]) {
+  constexpr int NR = IN_BF16 ? N / 8 : N / 4;
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (IN_BF16) {
+        x[8 * c + 2 * j] = u2f(w[j] << 16);
+        x[8 * c + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+      } else {
+        x[4 * c + j] = u2f(w[j]);
+      }
+    }
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void load_f32(const float* p, float (&x)[N]) {
 #pragma unroll
@@ -115,7 +147,7 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
   constexpr int G = D / NE;                      // lanes per vector
   constexpr int VPB = 256 / G;                   // vectors per block
   constexpr int NS = PREC == kPrecFP8 ? 1 : D / 32;   // scales per vector
-  __shared__ uint32_t amax_s[PREC == kPrecBF16 ? 1 : VPB * NS];
+  __shared__ __attribute__((aligned(16))) uint32_t amax_s[PREC == kPrecBF16 ? 1 : VPB * G];   // [vector][part]
   static_assert(NE == 16, "the split factors are computed for 16 elements per lane");
   const int nr = a.q_nr;                         // parts per vector with rotated elements
   const int tau = threadIdx.x;
@@ -136,8 +168,36 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
   const long long base = v * D + NE * g;
   const int e0 = NE * g;                         // first element of this lane
 
+  // Every load that does not need the token's position is issued first (the vector part, and
+  // for rotate-half RoPE its partner half a rotation away in the same vector, read from memory
+  // — the partner lane's cache lines — rather than exchanged between lanes); the position
+  // lookup follows while they are in flight, then the angle table.
+  const bool rot_half = a.R > 0 && !a.interleaved && e0 >= D - a.R;   // uniform per wave
+  const bool first = e0 < D - a.R / 2;           // first half of the rotated dims
+  // document boundaries for the position lookup, one per lane (fewer than 64 documents)
+  const int lane = threadIdx.x & 63;
+  const bool wave_cu = a.R > 0 && a.B < 64;
+  const int cb = wave_cu && lane < a.B ? __ldg(a.cu + lane) : 0;
+  RawIn<IN_BF16, NE> rx, rp;
+  load_raw<IN_BF16, NE>(a.q_in, base, rx);
+  if (rot_half) load_raw<IN_BF16, NE>(a.q_in, base + (first ? a.R / 2 : -(a.R / 2)), rp);
+  int pos = 0;
+  if (a.R > 0) {
+    // a wave's vectors normally belong to one token: its document is then the last b with
+    // cu[b] <= t, found by a ballot over the boundaries loaded above (else a binary search)
+    const int t0 = __builtin_amdgcn_readfirstlane(t);
+    int tpos;
+    if (wave_cu && __all(t == t0)) {
+      const unsigned long long m = __ballot(lane < a.B && cb <= t0);
+      const int b = m ? 63 - __clzll((long long)m) : 0;
+      tpos = max(0, t0 - clampi(__builtin_amdgcn_readlane(cb, b), 0, a.T));
+    } else {
+      tpos = token_position(a.cu, a.B, a.T, t);
+    }
+    pos = min(tpos, a.max_pos - 1);
+  }
   float x[NE];
-  load_in<IN_BF16, NE>(a.q_in, base, x);
+  convert_in<IN_BF16, NE>(rx, x);
   if (!IN_BF16 && !a.rope_fp32) {
 #pragma unroll
     for (int j = 0; j < NE; ++j) x[j] = bf16_round(x[j]);
@@ -145,11 +205,6 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
 
   if (a.R > 0) {
     const int rs = D - a.R;
-    // a wave's vectors normally belong to one token: then its position is found once,
-    // on the scalar unit
-    const int t0 = __builtin_amdgcn_readfirstlane(t);
-    const int tpos = __all(t == t0) ? token_position(a.cu, a.B, a.T, t0) : token_position(a.cu, a.B, a.T, t);
-    const int pos = min(tpos, a.max_pos - 1);
     const int half = a.R / 2;
     const float* crow = a.cos_t + (long long)pos * half;
     const float* srow = a.sin_t + (long long)pos * half;
@@ -165,13 +220,10 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
           x[j + 1] = x2 * c + x1 * s;
         }
       }
-    } else if (e0 >= rs) {
-      // rotate-half (NE divides rope_dim / 2, so a lane's elements rotate together): the
-      // partner elements, half a rotation away in the same vector, are read from memory
-      // (the partner lane's cache lines) rather than exchanged between lanes
-      const bool first = e0 < rs + half;
+    } else if (rot_half) {
+      // rotate-half (NE divides rope_dim / 2, so a lane's elements rotate together)
       float p[NE];
-      load_in<IN_BF16, NE>(a.q_in, base + (first ? half : -half), p);
+      convert_in<IN_BF16, NE>(rp, p);
       if (!IN_BF16 && !a.rope_fp32) {
 #pragma unroll
         for (int j = 0; j < NE; ++j) p[j] = bf16_round(p[j]);
@@ -206,17 +258,20 @@ __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
       for (int c = 0; c < NE / 8; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
     }
   } else {
-    // magnitude maximum per scale block (the vector for FP8, 32 elements for MXFP8): lane
-    // maxima, combined in LDS (non-negative floats order like their bits)
-    const int slot = vb * NS + (NS == 1 ? 0 : e0 / 32);
-    for (int i = tau; i < VPB * NS; i += 256) amax_s[i] = 0u;
-    __syncthreads();
+    // magnitude maximum per scale block (the vector for FP8, 32 elements for MXFP8): each
+    // part's maximum to its own LDS slot, then the maximum over the block's parts
+    // (non-negative floats order like their bits)
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < NE; ++j) amax = fmaxf(amax, fabsf(x[j]));
-    atomicMax(&amax_s[slot], f2u(amax));
+    amax_s[vb * G + g] = f2u(amax);
     __syncthreads();
-    const int e = ue8m0_exponent(u2f(amax_s[slot]));
+    constexpr int PB = NS == 1 ? G : 32 / NE;    // parts per scale block
+    const int p0 = NS == 1 ? 0 : (g / PB) * PB;
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int q = 0; q < PB; ++q) mb = max(mb, amax_s[vb * G + p0 + q]);
+    const int e = ue8m0_exponent(u2f(mb));
     uint32_t w[NE / 4];
     e4m3_pack<NE>(x, e, w);
     if (valid) {
