@@ -49,6 +49,49 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def measure_peaks(prec, reps=5):
+    """Rates this device sustains, to set the kernels against beside the published peaks:
+    the scoring kernel's MFMA instruction with its operands in registers (dsa_bench_mfma,
+    1024 workgroups x 4 waves, four accumulator chains each), and HBM read-only and copy
+    sweeps over 1 GiB (dsa_bench_stream). Best of `reps` calls after a warm-up, each timed
+    with events on the stream the library launches on."""
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    dev = torch.device("cuda")
+
+    def best_rate(fn):
+        fn()
+        best = 0.0
+        for _ in range(reps):
+            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.record()
+            work = fn()
+            en.record()
+            en.synchronize()
+            best = max(best, work / (st.elapsed_time(en) * 1e-3))
+        return best
+
+    blocks = 1024
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    iters = 8000 if prec == "bf16" else 4000
+    mfma = best_rate(lambda: dsa.bench_mfma(prec, blocks, iters, out))
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    read = best_rate(lambda: dsa.bench_stream(src, dst, copy=False))
+    copy = best_rate(lambda: dsa.bench_stream(src, dst, copy=True))
+
+    def torch_copy():
+        dst.copy_(src)
+        return 2 * src.numel()
+    tcopy = best_rate(torch_copy)
+    del src, dst
+    return {"mfma_tflops": round(mfma / 1e12, 1), "mfma_dtype": prec, "hbm_read_gbps": round(read / 1e9, 1),
+            "hbm_copy_gbps": round(copy / 1e9, 1), "hbm_torch_copy_gbps": round(tcopy / 1e9, 1),
+            "method": "dsa_bench_mfma (the scoring kernel's MFMA instruction, operands in registers), "
+                      "dsa_bench_stream (1 GiB read-only and copy sweeps) and torch's device copy of the same "
+                      "buffer; best of %d event-timed calls" % reps}
+
+
 def pair_count(cu, kp):
     L = np.diff(np.asarray(cu, np.int64))
     if kp == 1:
@@ -302,6 +345,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the on-device peak measurements")
     ap.add_argument("--copy-mb", type=int, default=0, help="calibration copy of this many MiB after timing")
     ap.add_argument("--fuse", action="store_true",
                     help="preprocess the queries inside the scoring kernel (dsa_index_score_fused) instead of in "
@@ -384,6 +428,17 @@ def main():
                      "frac": round(achieved * 1e12 / PEAK_FLOPS[prec], 4), "traffic": traffic},
         "kernels": kernels,
     }
+    if not args.no_peaks:
+        pk = measure_peaks(prec)
+        line["peaks_measured"] = pk
+        line["roofline"]["measured_peak"] = pk["mfma_tflops"]
+        line["roofline"]["frac_of_measured"] = round(achieved / pk["mfma_tflops"], 4)
+        hbm = max(pk["hbm_read_gbps"], pk["hbm_copy_gbps"], pk["hbm_torch_copy_gbps"])
+        for k in kernels.values():
+            if "gbps" in k:
+                k["frac_hbm_measured"] = round(k["gbps"] / hbm, 4)
+            if "tflops" in k and "heads" not in k:
+                k["frac_mfma_measured"] = round(k["tflops"] / pk["mfma_tflops"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

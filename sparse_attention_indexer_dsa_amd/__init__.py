@@ -26,7 +26,8 @@ import os
 import torch
 
 __all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "score_fused", "topk", "forward",
-           "forward_workspace_size", "selection_softmax", "sparse_attention", "library_path", "load", "PRECISIONS", "DsaError"]
+           "forward_workspace_size", "selection_softmax", "sparse_attention", "bench_mfma", "bench_stream",
+           "library_path", "load", "PRECISIONS", "DsaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libdsa_index.so"
@@ -82,6 +83,12 @@ def load():
     lib.dsa_index_score_fused.restype = i32
     lib.dsa_index_score_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32,
                                           i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+    lib.dsa_bench_mfma.restype = i32
+    lib.dsa_bench_mfma.argtypes = [i32, i32, i32, vp, vp]
+    lib.dsa_bench_mfma_flops.restype = ctypes.c_double
+    lib.dsa_bench_mfma_flops.argtypes = [i32, i32, i32]
+    lib.dsa_bench_stream.restype = i32
+    lib.dsa_bench_stream.argtypes = [vp, vp, sz, i32, vp]
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_last_error.argtypes = []
     _lib = lib
@@ -440,3 +447,29 @@ def sparse_attention(q, kv, indices, *, sm_scale, lengths=None, out=None, lse=No
                                         _ptr(lse), _stream(q.device))
     _check(st, "dsa_index_sparse_attention")
     return (out, lse) if return_lse else out
+
+
+def bench_mfma(precision, blocks, iters, out):
+    """Compute-only MFMA stream (dsa_bench_mfma) on the current stream; `out` is a float32
+    device tensor of blocks * 256 elements. Returns the flops of the call."""
+    lib = load()
+    prec = _prec(precision)
+    _need(out, "out", (torch.float32,))
+    if out.numel() < blocks * 256:
+        raise ValueError(f"out holds {out.numel()} floats, needs {blocks * 256}")
+    _check(lib.dsa_bench_mfma(prec, int(blocks), int(iters), _ptr(out), _stream(out.device)), "dsa_bench_mfma")
+    return float(lib.dsa_bench_mfma_flops(prec, int(blocks), int(iters)))
+
+
+def bench_stream(src, dst, copy):
+    """HBM sweep over src (dsa_bench_stream) on the current stream: copy to dst, or read only.
+    Returns the HBM bytes the call moves."""
+    lib = load()
+    _need(src, "src")
+    _need(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < (nbytes if copy else 16):
+        raise ValueError("dst is smaller than src (copy) or than 16 bytes (read)")
+    _check(lib.dsa_bench_stream(_ptr(src), _ptr(dst), nbytes, 1 if copy else 0, _stream(src.device)),
+           "dsa_bench_stream")
+    return 2 * nbytes if copy else nbytes

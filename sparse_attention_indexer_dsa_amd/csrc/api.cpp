@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <string>
 
+#include "../../include/dsa_bench.h"
 #include "../../include/dsa_index.h"
 #include "launch.h"
 
@@ -494,6 +495,34 @@ dsa_status_t dsa_index_sparse_attention(const void* q, const void* kv, const int
   hipError_t e = dsa::launch_sparse_mla(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), indices,
                                         lengths, T, H, S, topk, sm_scale, static_cast<uint16_t*>(out), out_lse, stream);
   if (e != hipSuccess) return device_fail(e, "dsa_index_sparse_attention");
+  return DSA_OK;
+}
+
+dsa_status_t dsa_bench_mfma(dsa_precision_t precision, int32_t blocks, int32_t iters, float* out,
+                            hipStream_t stream) {
+  dsa_status_t st;
+  if ((st = check_precision((int)precision)) != DSA_OK) return st;
+  if (blocks < 1 || blocks > 65536 || iters < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "need 1 <= blocks <= 65536 and iters >= 1 (blocks=%d, iters=%d)", blocks, iters);
+  if (!out || !aligned(out, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "out must be a 4-byte aligned device pointer");
+  hipError_t e = dsa::launch_mfma_peak(precision == DSA_PREC_BF16 ? 0 : 1, blocks, iters, out, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_bench_mfma");
+  return DSA_OK;
+}
+
+double dsa_bench_mfma_flops(dsa_precision_t precision, int32_t blocks, int32_t iters) {
+  if (!valid_precision((int)precision) || blocks < 1 || iters < 1) return 0.0;
+  return dsa::mfma_peak_flops(precision == DSA_PREC_BF16 ? 0 : 1, blocks, iters);
+}
+
+dsa_status_t dsa_bench_stream(const void* src, void* dst, size_t bytes, int32_t copy, hipStream_t stream) {
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "src and dst must be 16-byte aligned device pointers");
+  if (copy != 0 && copy != 1) return fail(DSA_ERR_INVALID_ARGUMENT, "copy=%d must be 0 or 1", copy);
+  hipError_t e = dsa::launch_stream(src, dst, bytes, copy, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_bench_stream");
   return DSA_OK;
 }
 

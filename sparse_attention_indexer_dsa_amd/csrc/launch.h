@@ -69,4 +69,10 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
 // Largest row (candidates) the LDS top-k supports.
 constexpr int kTopkMaxCand = 32768;
 
+// On-device peak measurements (peak.hip)
+double mfma_peak_flops(int precision, int blocks, int iters);
+int mfma_peak_threads();
+hipError_t launch_mfma_peak(int precision, int blocks, int iters, float* out, hipStream_t st);
+hipError_t launch_stream(const void* src, void* dst, size_t bytes, int copy, hipStream_t st);
+
 }  // namespace dsa

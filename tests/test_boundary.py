@@ -1,5 +1,4 @@
-"""The C ABI library on the CPU: it loads, exports every function include/dsa_index.h
-declares, sizes workspaces on the host, and rejects invalid or unsupported arguments with
+"""The C ABI library on the CPU: it loads, exports every function include/*.h declares, sizes workspaces on the host, and rejects invalid or unsupported arguments with
 the documented status codes before touching any device (no compute call is made here)."""
 
 import ctypes
@@ -10,6 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa_index.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "dsa_bench.h")
 
 
 @pytest.fixture(scope="module")
@@ -27,6 +27,33 @@ def test_exports_every_declared_symbol(lib):
             "dsa_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_exports_measurement_symbols(lib):
+    text = open(BENCH_HEADER).read()
+    names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
+    assert {"dsa_bench_mfma", "dsa_bench_mfma_flops", "dsa_bench_stream"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_measurement_validation(lib):
+    # host-side checks only: every call below is rejected before anything is launched
+    assert lib.dsa_bench_mfma(7, 8, 8, FAKE, None) == 2
+    assert lib.dsa_bench_mfma(1, 0, 8, FAKE, None) == 1
+    assert lib.dsa_bench_mfma(1, 8, 0, FAKE, None) == 1
+    assert lib.dsa_bench_mfma(1, 70000, 8, FAKE, None) == 1
+    assert lib.dsa_bench_mfma(1, 8, 8, None, None) == 1
+    assert lib.dsa_bench_stream(FAKE, FAKE, 0, 0, None) == 1
+    assert lib.dsa_bench_stream(FAKE, FAKE, 24, 0, None) == 1
+    assert lib.dsa_bench_stream(FAKE + 8, FAKE, 32, 0, None) == 1
+    assert lib.dsa_bench_stream(FAKE, None, 32, 1, None) == 1
+    assert lib.dsa_bench_stream(FAKE, FAKE, 32, 2, None) == 1
+    # flops per call: blocks x 4 waves x iters x 4 chains x flops per instruction
+    assert lib.dsa_bench_mfma_flops(0, 10, 100) == 10 * 4 * 100 * 4 * 32 * 32 * 16 * 2
+    assert lib.dsa_bench_mfma_flops(1, 10, 100) == 10 * 4 * 100 * 4 * 32 * 32 * 64 * 2
+    assert lib.dsa_bench_mfma_flops(2, 10, 100) == lib.dsa_bench_mfma_flops(1, 10, 100)
+    assert lib.dsa_bench_mfma_flops(5, 10, 100) == 0.0
 
 
 def test_workspace_size(lib):
