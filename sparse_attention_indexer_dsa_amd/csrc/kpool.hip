@@ -62,6 +62,39 @@ __global__ __launch_bounds__(256) void pool_offsets_kernel(const int32_t* __rest
   if (tid == 255) cu_pools[B] = part[255];
 }
 
+// The pooled key of pool gp (lane holds elements lane + 64 i) in the scoring precision.
+template <int D, int PREC>
+__device__ __forceinline__ void store_pooled(const KpoolLaunch& a, int gp, int lane, const float (&acc)[D / 64]) {
+  constexpr int E = D / 64;
+  const long long orow = (long long)gp * D;
+  if (PREC == kPrecBF16) {
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      reinterpret_cast<uint16_t*>(a.pooled)[orow + lane + 64 * i] = f32_to_bf16_rne(acc[i]);
+  } else if (PREC == kPrecFP8) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(acc[i]));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const int e = ue8m0_exponent(amax);
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      reinterpret_cast<uint8_t*>(a.pooled)[orow + lane + 64 * i] = (uint8_t)e4m3_encode(ldexpf(acc[i], -e));
+    if (lane == 0) a.pooled_scale[gp] = (uint8_t)(e + 127);
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {               // element lane + 64 i lies in block 2i + lane/32
+      float amax = fabsf(acc[i]);
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      const int e = ue8m0_exponent(amax);
+      reinterpret_cast<uint8_t*>(a.pooled)[orow + lane + 64 * i] = (uint8_t)e4m3_encode(ldexpf(acc[i], -e));
+      if ((lane & 31) == 0) a.pooled_scale[(long long)gp * (D / 32) + 2 * i + lane / 32] = (uint8_t)(e + 127);
+    }
+  }
+}
+
 template <int D, bool K_BF16, int PREC>
 __global__ __launch_bounds__(256) void kpool_kernel(KpoolLaunch a) {
   constexpr int E = D / 64;                      // elements per lane
@@ -105,33 +138,107 @@ __global__ __launch_bounds__(256) void kpool_kernel(KpoolLaunch a) {
     }
   }
 
-  const long long orow = (long long)gp * D;
-  if (PREC == kPrecBF16) {
+  store_pooled<D, PREC>(a, gp, lane, acc);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the row
+// broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// The same pooled keys with fewer than 64 documents and a compile-time pool size: every
+// wave finds its pool's document itself (lane b holds document b's boundaries and pool
+// count; a prefix sum gives cu_pools, which the first wave also writes, so no separate
+// launch precedes this one), and all gate, bias and key loads of the pool are issued
+// before any is used. The arithmetic is the generic kernel's, operation for operation.
+template <int D, bool K_BF16, int PREC, int KP>
+__global__ __launch_bounds__(256) void kpool_fast_kernel(KpoolLaunch a) {
+  constexpr int E = D / 64;                      // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int gp = blockIdx.x * 4 + threadIdx.x / 64;
+  int lo = 0, np = 0;
+  if (lane < a.B) {
+    lo = clampi(a.cu[lane], 0, a.S);
+    const int hi = clampi(a.cu[lane + 1], lo, a.S);
+    np = (hi - lo) / KP;
+  }
+  const int incl = wave_prefix_sum(np);
+  const int excl = incl - np;                    // cu_pools[lane] for lane < B
+  const int P = __builtin_amdgcn_readlane(incl, 63);
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    if (lane < a.B) a.cu_pools[lane] = excl;
+    if (lane == a.B) a.cu_pools[a.B] = P;
+  }
+  if (gp >= P) return;
+  // document of pool gp: the last b with cu_pools[b] <= gp (lane 0 always qualifies)
+  const unsigned long long m64 = __ballot(lane < a.B && excl <= gp);
+  const int b = 63 - __clzll((long long)m64);
+  const int start = __builtin_amdgcn_readlane(lo, b) + (gp - __builtin_amdgcn_readlane(excl, b)) * KP;
+
+  float z[KP], kv[KP][E];
 #pragma unroll
-    for (int i = 0; i < E; ++i)
-      reinterpret_cast<uint16_t*>(a.pooled)[orow + lane + 64 * i] = f32_to_bf16_rne(acc[i]);
-  } else if (PREC == kPrecFP8) {
-    float amax = 0.f;
+  for (int j = 0; j < KP; ++j) {
+    z[j] = bf16_to_f32(a.gate[start + j]) + a.bias[j];
+    const long long row = (long long)(start + j) * D;
 #pragma unroll
-    for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(acc[i]));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    const int e = ue8m0_exponent(amax);
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-      reinterpret_cast<uint8_t*>(a.pooled)[orow + lane + 64 * i] = (uint8_t)e4m3_encode(ldexpf(acc[i], -e));
-    if (lane == 0) a.pooled_scale[gp] = (uint8_t)(e + 127);
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; ++i) {               // element lane + 64 i lies in block 2i + lane/32
-      float amax = fabsf(acc[i]);
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-      const int e = ue8m0_exponent(amax);
-      reinterpret_cast<uint8_t*>(a.pooled)[orow + lane + 64 * i] = (uint8_t)e4m3_encode(ldexpf(acc[i], -e));
-      if ((lane & 31) == 0) a.pooled_scale[(long long)gp * (D / 32) + 2 * i + lane / 32] = (uint8_t)(e + 127);
+    for (int i = 0; i < E; ++i) {
+      const int e = lane + 64 * i;
+      kv[j][i] = K_BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[row + e])
+                        : reinterpret_cast<const float*>(a.k)[row + e];
     }
   }
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < KP; ++j) m = fmaxf(m, z[j]);
+  float sigma = 0.f;
+#pragma unroll
+  for (int j = 0; j < KP; ++j) sigma = j == 0 ? pexp(z[j] - m) : sigma + pexp(z[j] - m);
+  float acc[E];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const float aj = pexp(z[j] - m) / sigma;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float prod = aj * kv[j][i];
+      acc[i] = j == 0 ? prod : acc[i] + prod;
+    }
+  }
+  store_pooled<D, PREC>(a, gp, lane, acc);
+}
+
+template <int D, bool K_BF16, int PREC, int KP>
+void launch_fast(const KpoolLaunch& a, int blocks, hipStream_t st) {
+  hipLaunchKernelGGL((kpool_fast_kernel<D, K_BF16, PREC, KP>), dim3(blocks), dim3(256), 0, st, a);
+}
+
+template <int D, bool K_BF16, int PREC>
+void launch_fast_kp(const KpoolLaunch& a, int blocks, hipStream_t st) {
+  switch (a.kpool) {
+    case 2: launch_fast<D, K_BF16, PREC, 2>(a, blocks, st); break;
+    case 3: launch_fast<D, K_BF16, PREC, 3>(a, blocks, st); break;
+    default: launch_fast<D, K_BF16, PREC, 4>(a, blocks, st); break;
+  }
+}
+
+// One launch when every document fits a lane and kpool is 2, 3 or 4 (at least one
+// workgroup, which writes cu_pools even when there is no pool).
+template <int D, bool K_BF16>
+hipError_t launch_kp_fast(const KpoolLaunch& a, hipStream_t st) {
+  const int pmax = a.S / a.kpool;
+  const int blocks = pmax > 0 ? (pmax + 3) / 4 : 1;
+  switch (a.precision) {
+    case kPrecBF16: launch_fast_kp<D, K_BF16, kPrecBF16>(a, blocks, st); break;
+    case kPrecFP8: launch_fast_kp<D, K_BF16, kPrecFP8>(a, blocks, st); break;
+    default: launch_fast_kp<D, K_BF16, kPrecMXFP8>(a, blocks, st); break;
+  }
+  return hipGetLastError();
 }
 
 template <int D, bool K_BF16>
@@ -150,6 +257,10 @@ hipError_t launch_kp(const KpoolLaunch& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_kpool(const KpoolLaunch& a, hipStream_t st) {
+  if (a.B < 64 && a.kpool >= 2 && a.kpool <= 4) {
+    if (a.D == 128) return a.k_bf16 ? launch_kp_fast<128, true>(a, st) : launch_kp_fast<128, false>(a, st);
+    return a.k_bf16 ? launch_kp_fast<64, true>(a, st) : launch_kp_fast<64, false>(a, st);
+  }
   hipLaunchKernelGGL(pool_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu, a.B, a.S, a.kpool, a.cu_pools);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -111,11 +111,26 @@ def test_quantize_only(precision):
 
 @pytest.mark.parametrize("kp", [2, 3, 4])
 @pytest.mark.parametrize("tail", [True, False])
-@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+@pytest.mark.parametrize("precision", ["bf16", "fp8", "mxfp8"])
 def test_kpool(kp, tail, precision):
     cfg = dict(precision=precision, preprocess=precision != "bf16", layernorm=False, rope_dim=0, kpool=kp,
                kpool_tail=tail)
     _run_and_compare(50 + kp + 2 * tail, 64, 128, cfg, 6, docs=[37, 100, 5, 0, 130, 2, 3])
+
+
+@pytest.mark.parametrize("ndocs", [63, 64, 70])
+@pytest.mark.parametrize("kp", [2, 4, 5])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_kpool_many_documents(ndocs, kp, precision):
+    # Pooling takes one launch when the documents fit a wave's lanes (fewer than 64) and
+    # kpool is 2, 3 or 4, and a pool-offset launch plus a generic kernel otherwise: both
+    # sides of each bound, with empty, one-token and incomplete-pool documents.
+    rng = np.random.default_rng(600 + ndocs + kp)
+    docs = [int(x) for x in rng.integers(0, 24, ndocs)]
+    docs[3], docs[10], docs[-1] = 0, 1, kp - 1
+    cfg = dict(precision=precision, preprocess=precision != "bf16", layernorm=False, rope_dim=0, kpool=kp,
+               kpool_tail=True)
+    _run_and_compare(60 + ndocs + kp, 16, 64, cfg, 4, docs=docs)
 
 
 def test_kpool_after_preprocess():
