@@ -111,6 +111,12 @@ __device__ __forceinline__ bool tile_of_block(const ScoreArgs& a, int tq, int j,
   return true;
 }
 
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): the wave's
+// 64 lanes fill 1 KB at `lds` in lane order.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
 template <int PREC>
 using AOperand = typename std::conditional<PREC != kPrecBF16, i32x8, bf16x8>::type;
 
@@ -289,19 +295,32 @@ __device__ __forceinline__ void build_q_row(const ScoreArgs& a, long long vec, b
   }
 }
 
+// FP8 / MXFP8 operands (without the fused query preprocessing) stage key tiles by direct
+// buffer-to-LDS loads, which need no staging registers: with 32 or 64 heads the kernel then
+// fits 3 waves per SIMD.
 template <int H, int D, int PREC, bool FUSE>
-__global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (PREC != kPrecBF16 && !FUSE && H >= 32) ? 3 : 2)
+void score_kernel(ScoreArgs a) {
   constexpr bool kFP8 = PREC != kPrecBF16;
+  constexpr bool kDMA = kFP8 && !FUSE;
   constexpr int ES = kFP8 ? 1 : 2;               // operand bytes per element
   constexpr int RB = D * ES;                     // operand bytes per key row
-  constexpr int ROWB = RB + 16;                  // padded LDS row
+  // LDS key rows: padded by 16 bytes (register staging), or unpadded with the 16-byte chunks
+  // of row r permuted by c -> c ^ (r & SW) (direct loads), both so that the lanes reading one
+  // chunk of consecutive rows hit distinct banks
+  constexpr int ROWB = kDMA ? RB : RB + 16;
+  constexpr int SW = (RB / 16 >= 8 ? 8 : RB / 16) - 1;
   constexpr int KSTEPS = kFP8 ? D / 64 : D / 16; // MFMAs per 32x32 output block
   constexpr int TPW = 64 / H;                    // tokens per wave
   constexpr int TQ = 4 * TPW;                    // tokens per workgroup
   constexpr int NSB = D / 32;                    // 32-element scale blocks per row
 
   constexpr int NSBL = PREC == kPrecMXFP8 ? NSB : 1;   // key scales per LDS row
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kNK * ROWB];
+  // the two tile buffers are separate arrays: with direct loads into one while the other is
+  // read, the compiler can then tell that the reads need not wait for those loads
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[kNK * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds1[kNK * ROWB];
+  auto k_lds = [&](int b) -> uint8_t* { return b ? k_lds1 : k_lds0; };
   __shared__ uint8_t ks_lds[2][kFP8 ? kNK * NSBL : 1];
 
   const int tid = threadIdx.x;
@@ -422,24 +441,38 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
   const int lim = (int)max(0LL, min((long long)n_keys, (long long)a.S - kbase));   // stageable rows
   const uint8_t* kdoc = reinterpret_cast<const uint8_t*>(a.k_op) + (long long)kbase * RB;
   const uint8_t* sdoc = kFP8 ? a.k_scale + (long long)kbase * NSBL : nullptr;
+  // Direct loads: instruction it of wave w fills the tile's 16-byte slots
+  // (w NCH + it) * 64 + lane, slot s holding chunk (s % CH) ^ (row & SW) of row s / CH.
   int goff[NCH], lds_off[NCH];
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
-    const int ch = it * kThreads + tid;
-    const int row = ch / CH, cc = ch % CH;
-    goff[it] = row * RB + cc * 16;
-    lds_off[it] = row * ROWB + cc * 16;
+    if (kDMA) {
+      const int sl = (wv * NCH + it) * 64 + lane;
+      const int row = sl / CH, p = sl % CH;
+      goff[it] = row * RB + (p ^ (row & SW)) * 16;
+      lds_off[it] = 0;                         // unused: the destination is wave-uniform
+    } else {
+      const int ch = it * kThreads + tid;
+      const int row = ch / CH, cc = ch % CH;
+      goff[it] = row * RB + cc * 16;
+      lds_off[it] = row * ROWB + cc * 16;
+    }
   }
   const int sc_i = tid % NSC;                    // scale byte this thread stages (duplicates agree)
 
-  struct Stage { uint4 v[NCH]; uint32_t s; };
-  auto fetch = [&](Stage& st, int c0) {
+  struct Stage { uint4 v[kDMA ? 1 : NCH]; uint32_t s; };
+  // key tile c0 to registers, or (direct loads) to LDS buffer `dbuf`; its scales to registers
+  auto fetch = [&](Stage& st, int c0, int dbuf) {
     const int rem = max(0, lim - c0);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kdoc + (long long)c0 * RB, rem * RB);
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[it], 0, 0);
-      st.v[it] = make_uint4(v[0], v[1], v[2], v[3]);
+      if (kDMA) {
+        lds_dma16(kr, k_lds(dbuf) + (__builtin_amdgcn_readfirstlane(wv) * NCH + it) * 1024, goff[it]);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[it], 0, 0);
+        st.v[kDMA ? 0 : it] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
     }
     st.s = 0;
     if (kFP8) {
@@ -449,14 +482,25 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
   };
   auto put = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int it = 0; it < NCH; ++it) *reinterpret_cast<uint4*>(&k_lds[buf][lds_off[it]]) = st.v[it];
+    for (int it = 0; it < (kDMA ? 0 : NCH); ++it) *reinterpret_cast<uint4*>(k_lds(buf) + lds_off[it]) = st.v[it];
     if (kFP8) ks_lds[buf][sc_i] = (uint8_t)st.s;
   };
+  // LDS byte offsets of this lane's B-operand chunks in its row of column block 0 (rows
+  // nb * 32 + col of block nb add the constant nb * 32 * ROWB): chunks 4 kk + hl and
+  // 4 kk + 2 + hl (fp8), swizzled by the row's low bits with direct loads
+  int boff[kFP8 ? KSTEPS : 1][2];
+#pragma unroll
+  for (int kk = 0; kk < (kFP8 ? KSTEPS : 0); ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 4 * kk + 2 * h + hl;
+      boff[kk][h] = col * ROWB + ((kDMA ? (c ^ (col & SW)) : c) << 4);
+    }
 
   // ---- one 32-key column block: q.k on MFMA into acc
   typedef f32x16 Acc[2];
   auto mma = [&](int buf, int nb, Acc& acc) {
-    const uint8_t* kl = k_lds[buf];
+    const uint8_t* kl = k_lds(buf);
     const int krow_l = nb * 32 + col;            // key (LDS row) of this lane's B operand / C column
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -465,9 +509,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       if (kFP8) {
-        const uint8_t* src = kl + krow_l * ROWB + kk * 64 + 16 * hl;
-        uint4 v0 = *reinterpret_cast<const uint4*>(src);
-        uint4 v1 = *reinterpret_cast<const uint4*>(src + 32);
+        uint4 v0 = *reinterpret_cast<const uint4*>(kl + nb * 32 * ROWB + boff[kk][0]);
+        uint4 v1 = *reinterpret_cast<const uint4*>(kl + nb * 32 * ROWB + boff[kk][1]);
         i32x8 bop;
         bop[0] = v0.x; bop[1] = v0.y; bop[2] = v0.z; bop[3] = v0.w;
         bop[4] = v1.x; bop[5] = v1.y; bop[6] = v1.z; bop[7] = v1.w;
@@ -564,22 +607,45 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     mma(buf, 1, acc1);
     epilogue(acc0, c0);
   };
-  Stage sa, sb;
-  fetch(sa, 0);
-  fetch(sb, kNK);
-  put(sa, 0);
-  __syncthreads();
-  fetch(sa, 2 * kNK);
   int kt = 0;
-  for (; kt + 1 < n_tiles; kt += 2) {            // buffer 0 holds tile kt, sb tile kt+1, sa tile kt+2
-    compute(0, kt * kNK);
-    put(sb, 1);
+  if constexpr (kDMA) {
+    // Direct loads, one tile ahead: tile kt + 1 streams into the other LDS buffer while tile
+    // kt is multiplied out; the barrier that ends each tile first waits for this wave's loads
+    // (vmcnt 0), so the next tile is in LDS for every wave after it.
+    Stage st;
+    fetch(st, 0, 0);
+    put(st, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): the direct loads have landed
     __syncthreads();
-    fetch(sb, (kt + 3) * kNK);
-    compute(1, (kt + 1) * kNK);
+    for (; kt + 1 < n_tiles; kt += 2) {          // buffer 0 holds tile kt
+      fetch(st, (kt + 1) * kNK, 1);
+      compute(0, kt * kNK);
+      put(st, 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      fetch(st, (kt + 2) * kNK, 0);
+      compute(1, (kt + 1) * kNK);
+      put(st, 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+  } else {
+    Stage sa, sb;
+    fetch(sa, 0, 0);
+    fetch(sb, kNK, 0);
     put(sa, 0);
     __syncthreads();
-    fetch(sa, (kt + 4) * kNK);
+    fetch(sa, 2 * kNK, 0);
+    for (; kt + 1 < n_tiles; kt += 2) {          // buffer 0 holds tile kt, sb tile kt+1, sa tile kt+2
+      compute(0, kt * kNK);
+      put(sb, 1);
+      __syncthreads();
+      fetch(sb, (kt + 3) * kNK, 0);
+      compute(1, (kt + 1) * kNK);
+      put(sa, 0);
+      __syncthreads();
+      fetch(sa, (kt + 4) * kNK, 0);
+    }
   }
   if (kt < n_tiles) compute(0, kt * kNK);        // odd tile count: the last tile is in buffer 0
   epilogue(acc1, n_tiles * kNK - 32);
