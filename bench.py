@@ -324,6 +324,9 @@ def ingest_pmc(fetch_db, write_db, copy_mb, workload):
         if not score or not copy:
             raise SystemExit(f"{db}: no {counter} records for the scoring or the copy kernel")
         copy_kib = max(copy)                       # the calibration copy is the largest copy
+        if any(1024.0 < v < 0.99 * copy_kib for v in copy):
+            raise SystemExit(f"{db}: copies of different sizes; record the counters with --no-peaks so the "
+                             "calibration copy is the only large one")
         factor = copy_mb * 1024.0 / copy_kib
         res[counter] = {"kib_per_launch": float(np.mean(score)), "copy_kib": copy_kib, "factor": factor,
                         "bytes_per_launch": float(np.mean(score)) * 1024.0 * factor}

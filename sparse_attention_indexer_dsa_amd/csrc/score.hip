@@ -306,10 +306,14 @@ void score_kernel(ScoreArgs a) {
   constexpr int ES = kFP8 ? 1 : 2;               // operand bytes per element
   constexpr int RB = D * ES;                     // operand bytes per key row
   // LDS key rows: padded by 16 bytes (register staging), or unpadded with the 16-byte chunks
-  // of row r permuted by c -> c ^ (r & SW) (direct loads), both so that the lanes reading one
-  // chunk of consecutive rows hit distinct banks
+  // of row r permuted by c -> c ^ swz(r) (direct loads), both so that the 16 lanes that LDS
+  // serves together (16 consecutive rows, one chunk each: 256 bytes over the 64 banks) hit
+  // distinct banks: rows 256 / RB apart share a bank window, swz(r) = (r / (256 / RB)) mod
+  // (RB / 16) tells them apart
   constexpr int ROWB = kDMA ? RB : RB + 16;
-  constexpr int SW = (RB / 16 >= 8 ? 8 : RB / 16) - 1;
+  constexpr int CHR = RB / 16;                   // 16-byte chunks per row
+  constexpr int RPW = 256 / RB > 0 ? 256 / RB : 1;   // rows per 256-byte bank window
+  auto swz = [](int r) { return (r / RPW) & (CHR - 1); };
   constexpr int KSTEPS = kFP8 ? D / 64 : D / 16; // MFMAs per 32x32 output block
   constexpr int TPW = 64 / H;                    // tokens per wave
   constexpr int TQ = 4 * TPW;                    // tokens per workgroup
@@ -442,14 +446,14 @@ void score_kernel(ScoreArgs a) {
   const uint8_t* kdoc = reinterpret_cast<const uint8_t*>(a.k_op) + (long long)kbase * RB;
   const uint8_t* sdoc = kFP8 ? a.k_scale + (long long)kbase * NSBL : nullptr;
   // Direct loads: instruction it of wave w fills the tile's 16-byte slots
-  // (w NCH + it) * 64 + lane, slot s holding chunk (s % CH) ^ (row & SW) of row s / CH.
+  // (w NCH + it) * 64 + lane, slot s holding chunk (s % CH) ^ swz(row) of row s / CH.
   int goff[NCH], lds_off[NCH];
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
     if (kDMA) {
       const int sl = (wv * NCH + it) * 64 + lane;
       const int row = sl / CH, p = sl % CH;
-      goff[it] = row * RB + (p ^ (row & SW)) * 16;
+      goff[it] = row * RB + (p ^ swz(row)) * 16;
       lds_off[it] = 0;                         // unused: the destination is wave-uniform
     } else {
       const int ch = it * kThreads + tid;
@@ -494,7 +498,7 @@ void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = 4 * kk + 2 * h + hl;
-      boff[kk][h] = col * ROWB + ((kDMA ? (c ^ (col & SW)) : c) << 4);
+      boff[kk][h] = col * ROWB + ((kDMA ? (c ^ swz(col)) : c) << 4);   // swz(nb * 32 + col) = swz(col)
     }
 
   // ---- one 32-key column block: q.k on MFMA into acc
