@@ -12,7 +12,9 @@
 // document; each wave owns 64 MFMA rows = 64/H tokens x H heads, whose q operands stay in
 // registers for the whole sweep. The workgroup sweeps the document's causal keys in LDS
 // tiles of 64 keys (two 32-key MFMA column blocks). Workgroups are numbered from the end
-// of the documents so the longest causal rows start first.
+// of the documents so the longest causal rows start first. FP8 and MXFP8 tiles go from HBM
+// straight into LDS (no staging registers), which lets those kernels run 3 waves per SIMD;
+// bf16 tiles pass through registers at 2 waves per SIMD.
 //
 // MFMA shapes (lane l, h = l/32):
 //   bf16  v_mfma_f32_32x32x16_bf16: A lane holds row l%32, k = 8h .. 8h+7.
@@ -593,11 +595,12 @@ void score_kernel(ScoreArgs a) {
     }
   };
 
-  // ---- sweep. Tiles alternate between two LDS buffers and two register stages: while
+  // ---- sweep. Tiles alternate between two LDS buffers. Register staging (bf16): while
   //      tile kt is multiplied out of one buffer, tile kt + 1 waits in registers for the other
-  //      buffer and tile kt + 2 is in flight, so a load has two tiles of work to land. Each
-  //      column block's epilogue runs while the next block's MFMAs execute (the first call
-  //      of a workgroup stores nothing: its candidates are negative). One barrier per tile.
+  //      buffer and tile kt + 2 is in flight, so a load has two tiles of work to land. Direct
+  //      loads (fp8, MXFP8): tile kt + 1 streams into the other buffer. Each column block's
+  //      epilogue runs while the next block's MFMAs execute (the first call of a workgroup
+  //      stores nothing: its candidates are negative). One barrier per tile.
   const int n_tiles = (n_keys + kNK - 1) / kNK;
   if (n_tiles == 0) return;
   Acc acc0, acc1;
