@@ -989,36 +989,35 @@ __global__ __launch_bounds__(NT) void topk_fallback_kernel(TopkArgs a) {
 // Launches kernel k (one of the two kernels at one shape) with `lds` bytes of dynamic LDS.
 // The dynamic LDS limit is raised only when a launch needs more than the default 64 KB, and
 // only to what it needs: the raised limit is what each workgroup reserves, so a blanket
-// 160 KB would leave one workgroup per CU. Done once per (kernel, device, size) and never
-// inside graph capture (it is not a stream operation).
-template <int NT>
-hipError_t launch_kernel(void (*k)(TopkArgs), const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
+// 160 KB would leave one workgroup per CU. Each kernel remembers, per device, the limit it
+// was last given, so repeated calls of one size (graph capture included) set nothing.
+template <int NT, void (*K)(TopkArgs)>
+hipError_t launch_kernel(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
   if (lds > 64 * 1024) {
     static std::mutex mu;
-    static const void* fn_of[64] = {nullptr};
     static size_t set_to[64] = {0};
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(mu);
-    if (device >= 64 || set_to[device] != lds || fn_of[device] != (const void*)k) {
-      e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (device >= 64 || set_to[device] != lds) {
+      e = hipFuncSetAttribute((const void*)K, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      if (device < 64) { set_to[device] = lds; fn_of[device] = (const void*)k; }
+      if (device < 64) set_to[device] = lds;
     }
   }
-  hipLaunchKernelGGL(k, dim3(grid), dim3(NT), lds, st, a);
+  hipLaunchKernelGGL(K, dim3(grid), dim3(NT), lds, st, a);
   return hipGetLastError();
 }
 
 template <int NT, int EPT>
 hipError_t launch_cfg(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
-  return launch_kernel<NT>(topk_kernel<NT, EPT>, a, lds, grid, st);
+  return launch_kernel<NT, topk_kernel<NT, EPT>>(a, lds, grid, st);
 }
 
 template <int NT, int EPT>
 hipError_t launch_fallback(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
-  return launch_kernel<NT>(topk_fallback_kernel<NT, EPT>, a, lds, grid, st);
+  return launch_kernel<NT, topk_fallback_kernel<NT, EPT>>(a, lds, grid, st);
 }
 
 int p2_of(int topk, int max_cand) {

@@ -134,8 +134,10 @@ def _run(docs, topk, kp, tail, seed):
 
 
 @pytest.mark.parametrize("L, topk", [(1000, 64), (2000, 256), (3000, 7), (4000, 512), (8000, 2048),
-                                     (16000, 2048), (32768, 2048), (1500, 2048)])
+                                     (16000, 2048), (32768, 2048), (1500, 2048), (9000, 6000)])
 def test_selection_patterns(L, topk):
+    # (9000, 6000): the 8192- and 16384-candidate shapes and the fallback launch each need
+    # more than 64 KB of LDS, so each raises its own limit
     _run([L], topk, 1, True, L + topk)
 
 
