@@ -103,16 +103,32 @@ def pair_count(cu, kp):
     return tot
 
 
+def device_inputs(inp, dev="cuda"):
+    """Device tensors of a generated workload: bf16 inputs (held as uint16 bit patterns) as
+    torch.bfloat16, everything else as it is."""
+    import torch
+
+    def put(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    d = {"q": put(inp["q"]), "k": put(inp["k"]), "w": put(inp["w"]), "cu": put(inp["cu_seqlens"])}
+    for name in ("gamma", "beta", "cos", "sin", "bias", "gate"):
+        if name in inp:
+            d[name] = put(inp[name])
+    return d
+
+
 def run_gpu(inp, steps, warmup, copy_mb=0, fuse=False, softmax=False, attn_heads=0):
     import torch
     import sparse_attention_indexer_dsa_amd as dsa
-    import parity
     dsa.load()
     dev = "cuda"
     T, H, D = inp["q"].shape
     prec, kp, topk, max_seqlen = inp["precision"], inp["kpool"], inp["topk"], inp["max_seqlen"]
     B = len(inp["docs"])
-    d = parity.gpu_inputs(inp)
+    d = device_inputs(inp, dev)
     esz = 2 if prec == "bf16" else 1
     nsb = {"bf16": 0, "fp8": 1, "mxfp8": D // 32}[prec]
     odt = torch.bfloat16 if prec == "bf16" else torch.uint8
@@ -295,6 +311,7 @@ def cpu_baseline(inp, budget_s):
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = int(blas[0]["num_threads"]) if blas else 1
     return {"value": total_pairs / est, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "blas_threads": cores, "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": (f"numpy fp64 oracle: full key side ({t_keys:.2f} s) + {done} random query rows "
                        f"({pairs} pairs, {t_rows:.2f} s), extrapolated to all {total_pairs} pairs"),
             "seconds": round(t_keys + t_rows, 2)}

@@ -32,6 +32,9 @@
  *     global key rows cu_seqlens[b] .. t.
  *   - The library never allocates, frees or synchronises the host inside a call. All
  *     work is enqueued on `stream` (asynchronous); results are ready when the stream is.
+ *     Calls may be captured into a HIP graph on one stream (tested: a captured step
+ *     replayed with new document boundaries matches eager calls). Capture that spreads the
+ *     calls of one step over several streams joined by events is not covered by tests.
  *   - Device-side data is trusted but never read out of bounds: a malformed cu_seqlens
  *     is clamped to [0, T] and documents longer than `max_seqlen` are truncated to it
  *     (their later rows see at most max_seqlen candidates); results are then unspecified.

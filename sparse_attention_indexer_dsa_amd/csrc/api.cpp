@@ -59,7 +59,7 @@ int row_stride(int max_cand) {
   return (c + 63) / 64 * 64;
 }
 
-constexpr size_t kMaxLds = 160 * 1024;
+constexpr size_t kMaxLds = dsa::kTopkMaxLds;
 
 }  // namespace
 

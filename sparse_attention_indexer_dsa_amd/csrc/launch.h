@@ -66,8 +66,10 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              int T, int H, int S, int topk, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t st);
 
-// Largest row (candidates) the LDS top-k supports.
+// Largest row (candidates) the LDS top-k supports, and the most LDS a workgroup can hold
+// (gfx950: 160 KB per CU).
 constexpr int kTopkMaxCand = 32768;
+constexpr size_t kTopkMaxLds = 160 * 1024;
 
 // On-device peak measurements (peak.hip)
 double mfma_peak_flops(int precision, int blocks, int iters);

@@ -141,7 +141,8 @@ __device__ __forceinline__ void load_f32(const float* p, float (&x)[N]) {
 // A block's VPB vectors are split by part: the threads first hold the parts that RoPE
 // touches (the last nr parts of every vector), then the others, so that whole waves either
 // rotate or not (a wave with both kinds would run both code paths). The scale's magnitude
-// maximum then spans waves: it is combined with LDS integer atomics.
+// maximum then spans waves: each part writes its maximum to its own LDS slot and, after one
+// barrier, every lane takes the maximum over the slots of its scale block.
 template <int D, bool IN_BF16, int PREC, int NE>
 __device__ __forceinline__ void preprocess_q(const PreArgs& a, int block) {
   constexpr int G = D / NE;                      // lanes per vector

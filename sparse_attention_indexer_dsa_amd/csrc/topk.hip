@@ -987,24 +987,30 @@ __global__ __launch_bounds__(NT) void topk_fallback_kernel(TopkArgs a) {
 }
 
 // Launches kernel k (one of the two kernels at one shape) with `lds` bytes of dynamic LDS.
-// The dynamic LDS limit is raised only when a launch needs more than the default 64 KB, and
-// only to what it needs: the raised limit is what each workgroup reserves, so a blanket
-// 160 KB would leave one workgroup per CU. Each kernel remembers, per device, the limit it
-// was last given, so repeated calls of one size (graph capture included) set nothing.
+// A launch above the default 64 KB of dynamic LDS needs the kernel's limit raised first.
+// The limit of a kernel only ever grows, to the largest size a launch of it has needed on
+// that device: a launch captured into a graph earlier keeps a limit at least as large as
+// its own when it is replayed after calls of smaller sizes. The check, the raise and the
+// launch happen under one lock, so another host thread cannot change the limit in between.
 template <int NT, void (*K)(TopkArgs)>
 hipError_t launch_kernel(const TopkArgs& a, size_t lds, int grid, hipStream_t st) {
-  if (lds > 64 * 1024) {
-    static std::mutex mu;
-    static size_t set_to[64] = {0};
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
+  if (lds <= 64 * 1024) {
+    hipLaunchKernelGGL(K, dim3(grid), dim3(NT), lds, st, a);
+    return hipGetLastError();
+  }
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static size_t raised[kDevices] = {0};
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  // devices past the table get the largest limit any launch can need, once per call
+  const size_t want = device < kDevices ? lds : kTopkMaxLds;
+  if (device >= kDevices || raised[device] < want) {
+    e = hipFuncSetAttribute((const void*)K, hipFuncAttributeMaxDynamicSharedMemorySize, (int)want);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    if (device >= 64 || set_to[device] != lds) {
-      e = hipFuncSetAttribute((const void*)K, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      if (device < 64) set_to[device] = lds;
-    }
+    if (device < kDevices) raised[device] = want;
   }
   hipLaunchKernelGGL(K, dim3(grid), dim3(NT), lds, st, a);
   return hipGetLastError();

@@ -58,9 +58,18 @@ def in_f32(a):
     return np.asarray(a, np.float32) if a.dtype == np.float32 else gen.bf16_bits_to_f32(a)
 
 
+def bf16_weights(inp):
+    """Switch a problem to bf16 per-head weights: the values are rounded to nearest-even bf16
+    (the oracle widens them exactly) and the library receives them as torch.bfloat16."""
+    inp["w"] = gen.bf16_bits_to_f32(gen.to_bf16_bits(inp["w"]))
+    inp["w_bf16"] = True
+    return inp
+
+
 def gpu_inputs(inp):
     """Device tensors of a generated problem."""
-    d = dict(q=dev_in(inp["q"]), k=dev_in(inp["k"]), w=dev(inp["w"]), cu=dev(inp["cu_seqlens"]))
+    w = dev_bf16(gen.to_bf16_bits(inp["w"])) if inp.get("w_bf16") else dev(inp["w"])
+    d = dict(q=dev_in(inp["q"]), k=dev_in(inp["k"]), w=w, cu=dev(inp["cu_seqlens"]))
     for name in ("gamma", "beta", "cos", "sin", "bias"):
         if name in inp:
             d[name] = dev(inp[name])
@@ -181,8 +190,9 @@ def compare_rows(g, ores, inp, cfg, topk, rows, sm_scale=1.0):
         b = doc[t]
         # all candidate scores from the workspace
         gs = np.asarray(g["ws"][t][:cand], dtype=np.float64)
-        bad = np.abs(gs - I) > tau * M + 1e-30
-        assert not bad.any(), (t, np.flatnonzero(bad)[:5], gs[bad][:5], I[bad][:5], M[bad][:5])
+        # written as "within tolerance" so that a NaN (which compares false) fails
+        ok = np.abs(gs - I) <= tau * M + 1e-30
+        assert np.all(np.isfinite(gs)) and ok.all(), (t, np.flatnonzero(~ok)[:5], gs[~ok][:5], I[~ok][:5], M[~ok][:5])
         # selection
         gsc = g["scores"][t]
         assert np.all(np.isneginf(gsc[nsel:])), t

@@ -92,6 +92,60 @@ def test_forward_fp32_inputs(precision):
     _check(inp, cfg, 16)
 
 
+@pytest.mark.parametrize("precision", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("H", [16, 32, 64])
+def test_forward_bf16_weights(precision, H):
+    # bf16 per-head weights through the fused path (query preprocessing in the scoring kernel)
+    cfg = dict(precision=precision, preprocess=True, layernorm=True, rope_dim=64, rope_fp32=True)
+    inp = gen.small(330 + H, DOCS, H, 128, layernorm=True, rope_dim=64)
+    inp["H"], inp["D"] = H, 128
+    parity.bf16_weights(inp)
+    _check(inp, cfg, 16)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("w_bf16", [False, True])
+def test_score_fused_direct(precision, w_bf16):
+    # dsa_index_score_fused on its own: the score rows it writes are those of
+    # dsa_index_preprocess + dsa_index_score (byte for byte) and within tolerance of the oracle,
+    # and the query operands it returns are the oracle's
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    H, D = 64, 128
+    cfg = dict(precision=precision, preprocess=True, layernorm=True, rope_dim=64, rope_fp32=False)
+    inp = gen.small(340 + w_bf16, DOCS, H, D, layernorm=True, rope_dim=64)
+    inp["H"], inp["D"] = H, D
+    if w_bf16:
+        parity.bf16_weights(inp)
+    d = parity.gpu_inputs(inp)
+    T, ms = inp["q"].shape[0], inp["max_seqlen"]
+    ops = dsa.preprocess(d["q"], d["k"], d["cu"], ln_gamma=d["gamma"], ln_beta=d["beta"], ln_eps=gen.LN_EPS,
+                         rope_cos=d["cos"], rope_sin=d["sin"], rope_dim=64, rope_fp32=False, precision=precision)
+    n = dsa.workspace_size(T, ms, 1, 1, H, D, len(inp["docs"]), precision)
+    ws_two = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    ws_one = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dsa.score(ops["q_op"], ops["k_op"], d["w"], d["cu"], ms, ws_two, q_scale=ops.get("q_scale"),
+              k_scale=ops.get("k_scale"), precision=precision)
+    got_ops = {"q_op": torch.empty_like(ops["q_op"])}
+    if precision != "bf16":
+        got_ops["q_scale"] = torch.empty_like(ops["q_scale"])
+    dsa.score_fused(d["q"], ops["k_op"], d["w"], d["cu"], ms, ws_one, k_scale=ops.get("k_scale"),
+                    rope_cos=d["cos"], rope_sin=d["sin"], rope_dim=64, rope_fp32=False, precision=precision,
+                    out_operands=got_ops)
+    torch.cuda.synchronize()
+    assert torch.equal(ws_one, ws_two), "fused score rows differ from the two-call path"
+    o = parity.oracle_operands(inp, cfg)
+    assert np.array_equal(parity.host(got_ops["q_op"]).view(np.uint8), np.asarray(o["q_op"]).view(np.uint8))
+    if precision != "bf16":
+        assert np.array_equal(parity.host(got_ops["q_scale"]), o["q_scale"])
+    ws = parity.workspace_scores(parity.host(ws_one), T, ms, 1)
+    ores = orc.score_rows(o["q_deq"], o["k_deq"], inp["w"].astype(np.float64), inp["cu_seqlens"])
+    tau = parity.TAU[precision]
+    for t, (I, M) in ores.items():
+        g = ws[t, :I.size].astype(np.float64)
+        assert np.all(np.abs(g - I) <= tau * M + 1e-30), t      # false for a NaN
+
+
 def test_forward_full_workload():
     # the 2 x 4096, H=64, D=128, fp8 workload: one call against the two-call path, all rows
     inp = gen.workload(3)

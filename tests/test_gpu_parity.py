@@ -36,8 +36,10 @@ def _problem(seed, H, D, cfg, docs=DOCS):
     return inp
 
 
-def _run_and_compare(seed, H, D, cfg, topk, docs=DOCS, sm_scale=1.0):
+def _run_and_compare(seed, H, D, cfg, topk, docs=DOCS, sm_scale=1.0, w_bf16=False):
     inp = _problem(seed, H, D, cfg, docs)
+    if w_bf16:
+        parity.bf16_weights(inp)
     g = parity.gpu_pipeline(inp, cfg, topk, sm_scale=sm_scale)
     o = parity.oracle_operands(inp, cfg)
     kp = cfg.get("kpool", 1)
@@ -107,6 +109,24 @@ def test_quantize_only(precision):
     # no LayerNorm, no RoPE: bf16 inputs quantised for scoring
     cfg = dict(precision=precision, preprocess=True, layernorm=False, rope_dim=0)
     _run_and_compare(31, 64, 128, cfg, 32)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_weights(precision, H, D):
+    # per-head weights passed as bf16 (PR 8403, codex review finding 3: the weights stay BF16),
+    # widened exactly by the scoring kernel
+    cfg = dict(precision=precision, preprocess=True, layernorm=True, rope_dim=64 if D == 128 else 32,
+               rope_fp32=True)
+    _run_and_compare(400 + H + D, H, D, cfg, 16, w_bf16=True)
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_bf16_weights_raw_bf16_and_kpool(H):
+    _run_and_compare(430 + H, H, 128, dict(precision="bf16", preprocess=False), 8, w_bf16=True)
+    _run_and_compare(440 + H, H, 128, dict(precision="bf16", preprocess=False, kpool=4, kpool_tail=True), 5,
+                     docs=[37, 100, 5, 0, 130, 2, 3], w_bf16=True)
 
 
 @pytest.mark.parametrize("kp", [2, 3, 4])

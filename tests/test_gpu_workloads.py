@@ -22,10 +22,12 @@ def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
-def test_workload(wid):
+@pytest.mark.parametrize("wid, w_bf16", [(1, False), (2, False), (3, False), (4, False), (5, False), (3, True)])
+def test_workload(wid, w_bf16):
     import torch
     inp = gen.workload(wid)
+    if w_bf16:      # the same workload with the per-head weights passed as bf16
+        parity.bf16_weights(inp)
     cfg = parity.config_of(inp)
     topk, kp = inp["topk"], inp["kpool"]
     T = inp["q"].shape[0]
