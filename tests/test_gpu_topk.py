@@ -188,3 +188,49 @@ def test_selection_outlier_rows(L, topk, big):
         n = sel.size
         assert np.array_equal(host["indices"][t][:n].astype(np.int64), sel), t
         assert np.array_equal(host["scores"][t][:n].astype(np.float64), s), t
+
+
+def test_lds_limit_kept_for_captured_launch():
+    # A top-k call whose 16384-candidate launch needs ~140 KB of dynamic LDS is captured into
+    # a graph (one stream); then an eager call needing ~74 KB in the same kernels runs; the
+    # graph is replayed (twice, with eager work between). The kernels' LDS limit must still
+    # cover the captured launch: every replay equals the eager result of the captured call,
+    # byte for byte. The smaller call's selection is the prefix of the larger one's (both
+    # are ordered by score descending, then index ascending).
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    L, big, small = 9000, 8500, 6000
+    stride = (L + 63) // 64 * 64
+    gen_t = torch.Generator(device="cuda").manual_seed(123)
+    flat = torch.randn(L * stride + 64, generator=gen_t, device="cuda", dtype=torch.float32) * 3.0
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    ref = dsa.topk(flat, L, cu, L, big)
+    torch.cuda.synchronize()
+    out = dsa._alloc_outputs(None, L, big, 1, "cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dsa.topk(flat, L, cu, L, big, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dsa.topk(flat, L, cu, L, big, out=out)
+    for rep in range(2):
+        for n in out:
+            out[n].fill_(7)
+        sm = dsa.topk(flat, L, cu, L, small)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in ("indices", "scores", "lengths"):
+            assert torch.equal(out[n].view(torch.int32), ref[n].view(torch.int32)), (rep, n)
+        assert torch.equal(sm["indices"], ref["indices"][:, :small]), rep
+        assert torch.equal(sm["scores"].view(torch.int32), ref["scores"][:, :small].view(torch.int32)), rep
+    # the captured call's rows against the oracle on a few rows
+    host_i, host_s = ref["indices"].cpu().numpy(), ref["scores"].cpu().numpy()
+    for t in (0, 4000, 8191, 8192, 8600, L - 1):
+        v = flat[t * stride:t * stride + t + 1].cpu().numpy().astype(np.float64)
+        sel, s = orc.topk_row(v, big)
+        assert np.array_equal(host_i[t][:sel.size].astype(np.int64), sel), t
+        assert np.array_equal(host_s[t][:sel.size].astype(np.float64), s), t
