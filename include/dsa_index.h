@@ -234,6 +234,36 @@ dsa_status_t dsa_index_topk(
     int32_t* out_indices, float* out_scores, int32_t* out_lengths, int32_t* out_pool_indices,
     hipStream_t stream);
 
+/*
+ * dsa_index_score_topk_noalloc - dsa_index_score_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, outputs and errors without `workspace` /
+ * `workspace_bytes`. The score rows go to a fixed scratch array the library holds on every
+ * GPU it runs on, DSA_NOALLOC_SCRATCH_BYTES bytes, from the time its code is loaded on the
+ * device until the process ends. The call allocates and frees nothing.
+ *   - Sizes: the call needs dsa_index_workspace_size(T, H, D, num_seqs, max_seqlen, topk,
+ *     kpool, precision) bytes of scratch (T rows times the row stride times 4, plus 256):
+ *     e.g. 8192 rows of 4096 candidates. A larger problem returns DSA_ERR_UNSUPPORTED
+ *     before anything is enqueued; use dsa_index_score_topk with a workspace instead.
+ *   - Sharing: every call on one GPU uses that GPU's one array, which keeps the last call's
+ *     contents (nothing in it needs to start at zero). Calls that overlap on one GPU (on
+ *     different streams, or from several host threads without ordering) race on it and
+ *     give undefined results: order them on one stream.
+ *   - The array's device address is looked up once per device, on the first call made
+ *     with that device current.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)134221824) /* 128 MiB + 4 KiB */
+dsa_status_t dsa_index_score_topk_noalloc(
+    const void* q_op, const uint8_t* q_scale,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools, int32_t kpool_tail,
+    int32_t topk, float sm_scale, dsa_precision_t precision,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths,
+    int32_t* out_pool_indices, hipStream_t stream);
+
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* dsa_last_error(void);
 

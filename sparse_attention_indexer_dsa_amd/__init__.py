@@ -25,7 +25,8 @@ import os
 
 import torch
 
-__all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score", "score_fused", "topk", "forward",
+__all__ = ["preprocess", "kpool", "workspace_size", "score_topk", "score_topk_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "score", "score_fused", "topk", "forward",
            "forward_workspace_size", "selection_softmax", "sparse_attention", "bench_mfma", "bench_stream",
            "library_path", "load", "PRECISIONS", "DsaError"]
 
@@ -66,6 +67,9 @@ def load():
     lib.dsa_index_score_topk.restype = i32
     lib.dsa_index_score_topk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32, vp,
                                          i32, i32, f32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_index_score_topk_noalloc.restype = i32
+    lib.dsa_index_score_topk_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
+                                                 vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]
     lib.dsa_index_score.restype = i32
     lib.dsa_index_score.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32, vp,
                                     f32, i32, vp, sz, vp]
@@ -267,6 +271,47 @@ def score_topk(q_op, k_op, w, cu_seqlens, max_seqlen, topk, *, q_scale=None, k_s
         _ptr(out.get("pool_indices")), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(dev))
     _check(st, "dsa_index_score_topk")
+    return out
+
+
+# Bytes of the fixed device scratch score_topk_noalloc uses (DSA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = (128 << 20) + 4096
+
+
+def score_topk_noalloc(q_op, k_op, w, cu_seqlens, max_seqlen, topk, *, out, q_scale=None, k_scale=None,
+                       precision="bf16", sm_scale=1.0, kpool=1, cu_pools=None, kpool_tail=True):
+    """``score_topk`` through dsa_index_score_topk_noalloc: no workspace; the score rows go to
+    the library's fixed device scratch (NOALLOC_SCRATCH_BYTES per GPU, shared by every call
+    on that GPU; calls that overlap on one GPU race). ``out`` must hold preallocated
+    'indices', 'scores', 'lengths' (and 'pool_indices' or not, when kpool > 1), shaped as
+    ``score_topk`` returns them; nothing is allocated here."""
+    lib = load()
+    prec = _prec(precision)
+    T, H, D = q_op.shape
+    S = k_op.shape[0]
+    for name, t in (("q_op", q_op), ("k_op", k_op), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale),
+                    ("cu_pools", cu_pools)):
+        _need(t, name)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,))
+    if w.dtype not in _DTYPES:
+        raise ValueError(f"w must be bf16 or fp32, got {w.dtype}")
+    width = topk if kpool == 1 else topk * kpool + kpool - 1
+    for name, shape, dt in (("indices", (T, width), torch.int32), ("scores", (T, topk), torch.float32),
+                            ("lengths", (T,), torch.int32)):
+        t = out.get(name)
+        if t is None or tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"out['{name}'] must be a preallocated {dt} tensor of shape {shape}")
+        _need(t, name)
+    pool = out.get("pool_indices") if kpool > 1 else None
+    if pool is not None and (tuple(pool.shape) != (T, topk) or pool.dtype != torch.int32):
+        raise ValueError(f"out['pool_indices'] must be an int32 tensor of shape {(T, topk)}")
+    _need(pool, "pool_indices")
+    st = lib.dsa_index_score_topk_noalloc(
+        _ptr(q_op), _ptr(q_scale), _ptr(k_op), _ptr(k_scale), _ptr(w), _DTYPES[w.dtype],
+        T, S, H, D, _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), int(kpool), _ptr(cu_pools),
+        int(bool(kpool_tail)), int(topk), float(sm_scale), prec, _ptr(out["indices"]), _ptr(out["scores"]),
+        _ptr(out["lengths"]), _ptr(pool), _stream(q_op.device))
+    _check(st, "dsa_index_score_topk_noalloc")
     return out
 
 

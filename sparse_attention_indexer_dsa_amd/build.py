@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdsa_index.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "preprocess.hip", "kpool.hip", "score.hip", "topk.hip", "softmax.hip", "attention.hip", "peak.hip"]
+SOURCES = ["api.cpp", "preprocess.hip", "kpool.hip", "score.hip", "topk.hip", "softmax.hip", "attention.hip", "peak.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -195,7 +195,7 @@ dsa_status_t check_geometry(int T, const int32_t* cu_seqlens, int num_seqs, int 
 
 dsa_status_t check_score_args(const void* q_op, const uint8_t* q_scale, const void* k_op, const uint8_t* k_scale,
                               const void* w, dsa_dtype_t w_dtype, int T, int S, int H, int D, int precision,
-                              const void* workspace) {
+                              const void* workspace, bool need_ws = true) {
   dsa_status_t st;
   if ((st = check_precision(precision)) != DSA_OK) return st;
   if (w_dtype != DSA_DTYPE_BF16 && w_dtype != DSA_DTYPE_FP32)
@@ -204,20 +204,22 @@ dsa_status_t check_score_args(const void* q_op, const uint8_t* q_scale, const vo
   if ((st = check_hd(H, D, true)) != DSA_OK) return st;
   if (T == 0) return DSA_OK;
   const bool fp8 = precision != DSA_PREC_BF16;
-  if (!q_op || !w || !workspace) return fail(DSA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!q_op || !w || (need_ws && !workspace)) return fail(DSA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if (S > 0 && !k_op) return fail(DSA_ERR_INVALID_ARGUMENT, "k_op is NULL");
   if (fp8 && (!q_scale || (S > 0 && !k_scale)))
     return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale/k_scale are required for an fp8 precision");
-  if (!aligned(q_op, 16) || (k_op && !aligned(k_op, 16)) || !aligned(workspace, 256) ||
+  if (!aligned(q_op, 16) || (k_op && !aligned(k_op, 16)) || (need_ws && !aligned(workspace, 256)) ||
       !aligned(w, w_dtype == DSA_DTYPE_FP32 ? 4 : 2))
     return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned buffer (operands 16 B, workspace 256 B, weights 4 B)");
   return DSA_OK;
 }
 
 dsa_status_t check_outputs(const int32_t* oi, const float* os, const int32_t* ol, const int32_t* op,
-                           const void* workspace) {
-  if (!oi || !os || !ol || !workspace) return fail(DSA_ERR_INVALID_ARGUMENT, "a required output pointer is NULL");
-  if (!aligned(oi, 4) || !aligned(os, 4) || !aligned(ol, 4) || (op && !aligned(op, 4)) || !aligned(workspace, 256))
+                           const void* workspace, bool need_ws = true) {
+  if (!oi || !os || !ol || (need_ws && !workspace))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "a required output pointer is NULL");
+  if (!aligned(oi, 4) || !aligned(os, 4) || !aligned(ol, 4) || (op && !aligned(op, 4)) ||
+      (need_ws && !aligned(workspace, 256)))
     return fail(DSA_ERR_INVALID_ARGUMENT, "misaligned output (4 B) or workspace (256 B)");
   return DSA_OK;
 }
@@ -318,6 +320,44 @@ dsa_status_t dsa_index_score_topk(
   if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk (score)");
   e = dsa::launch_topk(p, stream);
   if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk (top-k)");
+  return DSA_OK;
+}
+
+dsa_status_t dsa_index_score_topk_noalloc(
+    const void* q_op, const uint8_t* q_scale,
+    const void* k_op, const uint8_t* k_scale,
+    const void* w, dsa_dtype_t w_dtype,
+    int32_t T, int32_t S, int32_t H, int32_t D,
+    const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+    int32_t kpool, const int32_t* cu_pools, int32_t kpool_tail,
+    int32_t topk, float sm_scale, dsa_precision_t precision,
+    int32_t* out_indices, float* out_scores, int32_t* out_lengths,
+    int32_t* out_pool_indices, hipStream_t stream) {
+  static_assert(DSA_NOALLOC_SCRATCH_BYTES == dsa::kNoAllocScratchBytes, "scratch size of the header and the library");
+  dsa_status_t st;
+  if ((st = check_score_args(q_op, q_scale, k_op, k_scale, w, w_dtype, T, S, H, D, (int)precision, nullptr,
+                             false)) != DSA_OK)
+    return st;
+  if ((st = check_geometry(T, cu_seqlens, num_seqs, max_seqlen, kpool, cu_pools, topk, true)) != DSA_OK) return st;
+  if (T == 0) return DSA_OK;
+  if ((st = check_outputs(out_indices, out_scores, out_lengths, out_pool_indices, nullptr, false)) != DSA_OK)
+    return st;
+  const size_t need = dsa_index_workspace_size(T, H, D, num_seqs, max_seqlen, topk, kpool, precision);
+  if (need > dsa::kNoAllocScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_index_score_topk_noalloc: T=%d rows of max_seqlen=%d (kpool %d) need %zu bytes of scratch; "
+                "the fixed scratch holds %zu (use dsa_index_score_topk with a workspace)",
+                T, max_seqlen, kpool, need, dsa::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = dsa::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk_noalloc (scratch address)");
+  dsa::ScoreTopkLaunch p = make_launch(q_op, q_scale, k_op, k_scale, w, w_dtype, T, S, H, D, cu_seqlens, num_seqs,
+                                       max_seqlen, kpool, cu_pools, kpool_tail, topk, sm_scale, (int)precision,
+                                       out_indices, out_scores, out_lengths, out_pool_indices, scratch);
+  e = dsa::launch_score(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk_noalloc (score)");
+  e = dsa::launch_topk(p, stream);
+  if (e != hipSuccess) return device_fail(e, "dsa_index_score_topk_noalloc (top-k)");
   return DSA_OK;
 }
 

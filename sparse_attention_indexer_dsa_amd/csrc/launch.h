@@ -57,6 +57,11 @@ bool score_can_fuse_rope(int precision, int rope_dim, int interleaved);
 hipError_t launch_score(const ScoreTopkLaunch& p, hipStream_t st);
 hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st);
 
+// Fixed device scratch of the entry point that allocates nothing (noalloc.hip): the size of
+// the array on every GPU, and its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t(128) << 20) + 4096;
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_selection_softmax(const float* scores, int T, int topk, float* out, hipStream_t st);
 
 // Sparse absorbed-MLA attention: latent entry width (key) and value width, in elements.

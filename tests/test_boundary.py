@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"dsa_index_preprocess", "dsa_index_kpool", "dsa_index_workspace_size", "dsa_index_score_topk",
             "dsa_index_score", "dsa_index_topk", "dsa_index_forward", "dsa_index_forward_workspace_size",
             "dsa_index_score_fused", "dsa_index_selection_softmax", "dsa_index_sparse_attention",
-            "dsa_last_error"} <= set(names)
+            "dsa_last_error", "dsa_index_score_topk_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -97,6 +97,38 @@ def test_score_topk_validation(lib):
     assert _score(lib, wsb=10) == 3                         # everything valid but the workspace
     assert b"workspace" in lib.dsa_last_error()
     assert _score(lib, T=0) == 0                            # empty problem: nothing to do
+
+
+def test_score_topk_noalloc_validation(lib):
+    # host-side checks of the entry point that allocates nothing: the same argument checks as
+    # dsa_index_score_topk, then the fixed scratch bound, all before any device call
+    import sparse_attention_indexer_dsa_amd as dsa
+    text = open(HEADER).read()
+    assert f"DSA_NOALLOC_SCRATCH_BYTES ((size_t){dsa.NOALLOC_SCRATCH_BYTES})" in text
+
+    def call(**kw):
+        a = dict(q_op=FAKE, q_scale=FAKE, k_op=FAKE, k_scale=FAKE, w=FAKE, w_dtype=1, T=64, S=64, H=64, D=128,
+                 cu=FAKE, B=1, max_seqlen=64, kpool=1, cu_pools=None, tail=1, topk=8, sm=1.0, prec=0,
+                 oi=FAKE, os=FAKE, ol=FAKE, op=None)
+        a.update(kw)
+        return lib.dsa_index_score_topk_noalloc(
+            a["q_op"], a["q_scale"], a["k_op"], a["k_scale"], a["w"], a["w_dtype"], a["T"], a["S"], a["H"], a["D"],
+            a["cu"], a["B"], a["max_seqlen"], a["kpool"], a["cu_pools"], a["tail"], a["topk"], a["sm"], a["prec"],
+            a["oi"], a["os"], a["ol"], a["op"], None)
+    assert call(prec=7) == 2
+    assert call(H=48) == 2
+    assert call(topk=0) == 1
+    assert call(oi=None) == 1
+    assert call(q_op=FAKE + 8) == 1
+    assert call(T=0) == 0
+    # 8192 rows x 8192 candidates: 256 MiB of score rows > the 128 MiB + 4 KiB scratch
+    assert call(T=8192, S=8192, max_seqlen=8192) == 2
+    assert b"scratch" in lib.dsa_last_error()
+    # 16384 rows of 4 x 4096 tokens pooled by 4 (1024 candidates): 64 MiB, accepted up to the
+    # device call, which the host-only fake pointers never reach: check the size rule alone
+    need = lib.dsa_index_workspace_size(16384, 64, 128, 1, 4096, 8, 4, 0)
+    assert need <= dsa.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_index_workspace_size(8192, 64, 128, 2, 4096, 512, 1, 1) <= dsa.NOALLOC_SCRATCH_BYTES
 
 
 def test_score_only_candidate_bound(lib):
