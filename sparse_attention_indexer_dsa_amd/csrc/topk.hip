@@ -3,15 +3,16 @@
 // One workgroup per query row. Each thread holds 4-candidate chunks of the row, interleaved
 // across the workgroup, in registers; chunk groups past the row's last candidate are skipped
 // by every pass. A 2048-bin histogram linear in the score (LDS integer atomics) gives the bin
-// holding the topk-th largest key, whose few keys are then ranked exactly. Every candidate
-// above that key is taken and, among candidates equal to it, the lowest indices
-// (deterministic tie breaking, Megatron-LM PR 5992, "Key changes"). The same bins order the
-// selection: bin starts come from the histogram's suffix sums, every selected candidate goes
-// to its bin's range, and its exact rank inside the bin (score descending, index ascending)
-// gives its output position. A row whose bins do not separate the scores (a few outliers
-// stretching the range) is binned again over its selected region; rows neither level
-// separates (clustered or tied scores, no finite range) are finished by a second kernel: an
-// 11 + 11 + 10-bit radix select, a compaction by block prefix sums and a bitonic network.
+// holding the topk-th largest score, and its suffix sums give every bin its range of output
+// slots. Every candidate of that bin and of the bins above it is placed in its bin's range
+// with its score and index; its exact rank inside the bin (score descending, index
+// ascending) then gives its output position, and the threshold bin keeps only as many as the
+// selection still needs. Candidates equal to the last score taken are thus taken lowest
+// indices first (deterministic tie breaking, Megatron-LM PR 5992, "Key changes"). A row
+// whose bins do not separate the scores (a few outliers stretching the range) is binned
+// again over its selected region; rows neither level separates (clustered or tied scores,
+// no finite range) are finished by a second kernel: an 11 + 11 + 10-bit radix select, a
+// compaction by block prefix sums and a bitonic network.
 // Rows longer than
 // 4096 candidates run in launch shapes sized to them. No floating-point atomics; the result
 // does not depend on scheduling. Outputs are padded with -1 / -inf. For KPool (PR 7522,
@@ -338,8 +339,7 @@ __device__ __forceinline__ void scan_pass1_bins(uint32_t* hist, int krem, int* w
   __syncthreads();
 }
 
-constexpr int kValueList = 64;   // a threshold bin this small is resolved by counting
-constexpr int kBucketMax = 64;   // a selected pass-1 bin larger than this: bitonic ordering instead
+constexpr int kBucketMax = 64;   // a bin larger than this at or above the threshold: binned again, else the fallback
 constexpr int kHistSlots = 2048 + 16;   // pass-1 bins, then a slot that counts non-candidates
 constexpr int kFallbackGrid = 1024;     // workgroups of the fallback launch
 
@@ -406,25 +406,39 @@ struct RowOut {
   }
 };
 
-// Row of block j among the rows whose candidate count lies in [cls_lo, cls_hi] (documents in
-// order, positions ascending); false when j is past them. Candidate counts grow with the
-// position u in a document, so each document contributes the positions [ulo, uhi]; the
-// class holding max_cand also takes every position past it. One lane per document, 64
-// documents per step; every wave computes the same result.
+// Row of block j among the rows whose candidate count lies in [cls_lo, cls_hi]; false when
+// j is past them. Candidate counts grow with the position u in a document, so each document
+// contributes the positions [ulo, uhi]; the class holding max_cand also takes every position
+// past it. Blocks take the class's rows from the last (documents in reverse order, positions
+// descending), so that a document's longest rows start first and its short ones fill the
+// end of the launch. One lane per document, 64 documents per step; every wave computes the
+// same result.
 __device__ bool class_row(const TopkArgs& a, int j, int& t) {
   const int lane = threadIdx.x & 63;
   const int kp = a.kpool;
   const int ulo = a.cls_lo <= 0 ? 0 : a.cls_lo * kp - 1;
   const int uhi = a.cls_hi >= a.max_cand ? 0x7FFFFFFF : a.cls_hi * kp + kp - 2;
-  int base = 0;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int b = b0 + lane;
-    int n = 0, lo = 0;
+  auto rows_of = [&](int b, int& lo) {
+    int n = 0;
+    lo = 0;
     if (b < a.B) {
       lo = clampi(a.cu[b], 0, a.T);
       const int hi = clampi(a.cu[b + 1], lo, a.T);
       n = max(0, min(hi - lo - 1, uhi) - ulo + 1);
     }
+    return n;
+  };
+  int total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    int lo;
+    total += __builtin_amdgcn_readlane(wave_prefix_sum(rows_of(b0 + lane, lo)), 63);
+  }
+  if (j >= total) return false;
+  j = total - 1 - j;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    int lo;
+    const int n = rows_of(b0 + lane, lo);
     const int incl = wave_prefix_sum(n);
     const int tot = __builtin_amdgcn_readlane(incl, 63);
     const int r = j - base;
@@ -439,18 +453,20 @@ __device__ bool class_row(const TopkArgs& a, int j, int& t) {
   return false;
 }
 
+// At most 82 SGPRs (74 allocated besides VCC and the like): measured on the device, a wave
+// of more than about 90 keeps a SIMD at 7 waves or fewer, while the VGPRs here allow 8; the
+// few values that no longer fit move to VGPR lanes.
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_num_sgpr(82))) void topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  u64* selA = reinterpret_cast<u64*>(smem);                                  // [p2max]
+  u64* selA = reinterpret_cast<u64*>(smem);                                  // [p2max + kBucketMax]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);           // [kHistSlots]
   int* wsum = reinterpret_cast<int*>(hist + kHistSlots);                     // [32]
   int* misc = wsum + 32;                                                     // [16]
 
   const int tid = threadIdx.x;
-  const int topk = a.topk;
-  const int kp = a.kpool;
-  int t = blockIdx.x;
+  // rows from the last: a document's longest rows start first (see class_row)
+  int t = a.T - 1 - (int)blockIdx.x;
   if (a.cls_map && !class_row(a, blockIdx.x, t)) return;
   t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the row's values in scalar registers
   const RowInfo cur = row_info(a, t);
@@ -482,9 +498,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   };
   constexpr bool KEEP = EPT <= 16;
   float val[EPT];
-  uint32_t keyA[KEEP ? EPT : 1];
   int binA[KEEP ? EPT : 1];
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;   // over candidates only
+  // Range of the candidates, branch-free: slots past the row enter the minimum and maximum
+  // as a quiet NaN, which fminf / fmaxf ignore, and the product-sum `fin` (v * 0 summed;
+  // slots past the row load as +0 and add nothing) turns NaN as soon as one candidate is NaN
+  // or infinite.
+  float vlo = NAN, vhi = NAN, fin = 0.f;
   {
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.scores + (long long)t * a.stride, cand * 4);
     __attribute__((ext_vector_type(4))) uint32_t raw[NCH];
@@ -495,24 +514,21 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       if (!live(e)) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        val[4 * e + j] = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
-        const uint32_t k = keyof(val[4 * e + j]);
-        if (full(e)) {
-          kmax = max(kmax, k);
-          kmin = min(kmin, k);
-          if constexpr (KEEP) keyA[4 * e + j] = k;
-        } else if (idx(e, j) < cand) {
-          kmax = max(kmax, k);
-          kmin = min(kmin, k);
-          if constexpr (KEEP) keyA[4 * e + j] = k;
-        } else {
-          if constexpr (KEEP) keyA[4 * e + j] = 0u;
-        }
+        const float v = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
+        val[4 * e + j] = v;
+        const float m = idx(e, j) < cand ? v : NAN;
+        vlo = fminf(vlo, m);
+        vhi = fmaxf(vhi, m);
+        fin = __builtin_fmaf(v, 0.f, fin);
       }
     }
   }
 
-  // ---- key range of the row's candidates (max and min in one reduction)
+  // ---- range of the row's candidates as keys (max and min in one reduction; a thread with
+  //      no candidate contributes the neutral keys); a NaN or infinite score makes the
+  //      maximum key the largest one, so the row has no finite range
+  uint32_t kmin = vlo == vlo ? keyof(vlo) : 0xFFFFFFFFu;
+  uint32_t kmax = fin != fin ? 0xFFFFFFFFu : (vhi == vhi ? keyof(vhi) : 0u);
   block_minmax<NT>(kmin, kmax, wsum);
   const RowOut out(a, t, lo, b);
   if (cand == 0 || kmin == kmax) {
@@ -522,12 +538,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     return;
   }
 
-  uint32_t thr = kmin;   // every selected key is >= thr
-  int krem = cand;       // candidates equal to thr that are taken (lowest indices first)
-  int neq = 0;           // candidates equal to thr (known once the threshold is resolved)
-  bool resolved = cand <= topk;   // every candidate taken: no threshold needed
-  bool fast = false;     // order through the pass-1 bins (below)
-  int d1 = 0, a1 = 0;    // the threshold bin and the count of candidates in bins above it
+  bool fast = false;     // order through the bins (below)
+  int d1 = 0, a1 = 0, c1 = 0;   // the bin of the nsel-th largest score, candidates above it, in it
   const float vmin = key_score(kmin), vmax = key_score(kmax);
   const float span = vmax - vmin;
   const bool finite = span > 0.f && span < INFINITY;   // every candidate score finite, not all equal
@@ -545,11 +557,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     if (lvl == 0) return bin1(x);
     return bin1(x) >= dex ? bin2(x) : 2048 + (int)(threadIdx.x & 15);
   };
-  // Accessors over the two register layouts. With KEEP, slots past the row carry key 0 and a
-  // bin of 2048 or more, so no comparison below selects them without the `in` test.
-  auto keyat = [&](int e, int j) {
-    if constexpr (KEEP) return keyA[4 * e + j]; else return keyof(val[4 * e + j]);
-  };
+  // Bins over the two register layouts. With KEEP, slots past the row carry a bin of 2048 or
+  // more (a spare slot), so no bin test below selects them; without it the `in` test does.
   auto binat = [&](int e, int j) {
     if constexpr (KEEP) return binA[4 * e + j]; else return binof(val[4 * e + j]);
   };
@@ -570,8 +579,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     //      score to the largest score in bins up to the 17th largest's; the at most 16
     //      scores above that go to the top bin.
     if (pass == 1) {
-      // the second range, from exact keys: the smallest score in first-level bins >= d1
-      // and the largest in bins <= the 17th largest's bin
+      // the second range: the smallest score in first-level bins >= d1 and the largest in
+      // bins <= the 17th largest's
       const int dstar = misc[8];
       uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             if (in(e, j)) {
               int b1;
               if constexpr (KEEP) b1 = binA[4 * e + j]; else b1 = bin1(val[4 * e + j]);
-              const uint32_t k = keyat(e, j);
+              const uint32_t k = keyof(val[4 * e + j]);
               if (b1 >= d1) kmn = min(kmn, k);
               if (b1 <= dstar) kmx = max(kmx, k);
             }
@@ -599,12 +608,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       lvl = 1;
       __syncthreads();   // every thread has read misc and wsum above
     }
-    resolved = cand <= topk;
-    thr = kmin;
-    krem = cand;
-    neq = 0;
     for (int i = tid; i < kHistSlots / 4; i += NT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid == 0) { misc[5] = 0; misc[6] = 0; misc[8] = 2047; }
+    if (tid == 0) { misc[6] = 0; misc[8] = 2047; }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < NCH; ++e)
@@ -613,10 +618,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         for (int j = 0; j < 4; ++j) {
           int d = 2048 + (tid & 15);
           if (in(e, j)) {
-            // with KEEP the second level takes the score from its key (exact, -0 already
-            // folded), so the scores need not stay in registers past the first pass
             if constexpr (KEEP) d = lvl == 0 ? bin1(val[4 * e + j])
-                                             : (binA[4 * e + j] >= dex ? bin2(key_score(keyA[4 * e + j])) : d);
+                                             : (binA[4 * e + j] >= dex ? bin2(val[4 * e + j]) : d);
             else d = binof(val[4 * e + j]);
           }
           if constexpr (KEEP) binA[4 * e + j] = d;
@@ -627,155 +630,54 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     scan_pass1_bins<NT>(hist, nsel, wsum, misc, kBucketMax, 17);
     d1 = misc[0];
     a1 = misc[1];
-    const int c1 = misc[2];
-    const bool heavy = misc[6] != 0;
-    if (cand > topk && c1 <= kValueList) {
-      const int krem1 = topk - a1;
-      // the threshold bin's candidates to a list (order irrelevant), then one wave finds
-      // the krem1-th largest among them by counting over lane values
-      uint32_t* list = reinterpret_cast<uint32_t*>(selA);
-      {
-        uint32_t hit = 0;   // bit 4e+j: candidate in bin d1
-#pragma unroll
-        for (int e = 0; e < NCH; ++e)
-          if (live(e)) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hit |= (uint32_t)(cand_at(e, j) && binat(e, j) == d1) << (4 * e + j);
-          }
-        const int mine = __builtin_popcount(hit);
-        const int incl = wave_prefix_sum(mine);
-        const int wtot = __builtin_amdgcn_readlane(incl, 63);
-        int base = 0;
-        if ((tid & 63) == 63 && wtot > 0) base = atomicAdd(&misc[5], wtot);
-        int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
-        // the few hits, by their set bits; the key is recomputed from the row (in the cache)
-        const float* row = a.scores + (long long)t * a.stride;
-        while (hit) {
-          const int bpos = __builtin_ctz(hit);   // 4e + j
-          hit &= hit - 1;
-          list[pos++] = keyof(row[4 * ((bpos >> 2) * NT + tid) + (bpos & 3)] + 0.0f);
-        }
-      }
-      __syncthreads();
-      if (tid < 64) {
-        const uint32_t k = tid < c1 ? list[tid] : 0u;
-        int gt = 0, ge = 0;
-        for (int q = 0; q < c1; ++q) {
-          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)k, q);
-          gt += o > k;
-          ge += o >= k;
-        }
-        const bool hit = tid < c1 && gt < krem1 && krem1 <= ge;
-        const u64 m = __ballot(hit);
-        const int src = __ffsll((long long)m) - 1;
-        const uint32_t fk = __shfl(k, src, 64);
-        const int fg = __shfl(gt, src, 64);
-        const int fe = __shfl(ge, src, 64);
-        if (tid == 0) { misc[3] = (int)fk; misc[4] = krem1 - fg; misc[7] = fe - fg; }
-      }
-      __syncthreads();
-      thr = (uint32_t)misc[3];
-      krem = misc[4];
-      neq = misc[7];
-      resolved = true;
-    }
-    fast = resolved && !heavy;
+    c1 = misc[2];
+    // a bin at or above d1 of more than kBucketMax candidates (d1 itself included) is too
+    // crowded to rank inside
+    fast = misc[6] == 0;
   };
   if (finite) run_pass(0);
   if (finite && !fast) run_pass(1);
 
   if (fast) {
-    // ---- selection straight into bin order: bin d holds its candidates from slot
-    //      above(d) (the count in bins above it, the high half of its histogram word) on.
-    //      Scores above the threshold score are all taken; of those equal to it (all in bin
-    //      d1) the krem lowest indices, which needs their index order only when fewer are
-    //      taken than exist. Every score here is finite, so float comparisons order exactly
-    //      as the keys do.
-    const float vthr = key_score(thr);
-    auto is_eq = [&](int e, int j) {
-      if constexpr (KEEP) return keyA[4 * e + j] == thr; else return in(e, j) && val[4 * e + j] == vthr;
-    };
-    auto is_gt = [&](int e, int j) {
-      if constexpr (KEEP) return keyA[4 * e + j] > thr; else return in(e, j) && val[4 * e + j] > vthr;
-    };
-    auto is_ge = [&](int e, int j) {
-      if constexpr (KEEP) return keyA[4 * e + j] >= thr; else return in(e, j) && val[4 * e + j] >= vthr;
-    };
-    uint32_t eqtake = 0xFFFFFFFFu;   // bit 4e+j: a score equal to the threshold that is taken
-    if (neq > krem) {
-      // group e's equal keys come after all equal keys of groups < e; inside group e, thread
-      // order then position in the chunk. Fields of 16 bits, two groups per prefix sum.
-      eqtake = 0u;
-      int eq_before_group = 0;
+    // ---- every candidate of bins d1 .. 2047 (the selection, plus the rest of bin d1) takes
+    //      the next slot of its bin's range as (~key, bin, index): ascending order inside a
+    //      bin is score descending, then index ascending. The bin's word holds its first
+    //      slot (count in higher bins) in its high half since the scan. Every score here is
+    //      finite.
+    u64* ord = selA;
 #pragma unroll
-      for (int e2 = 0; e2 < NCH; e2 += 2) {
-        int c0 = 0, c1 = 0;
+    for (int e = 0; e < NCH; ++e)
+      if (live(e)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (live(e2)) c0 += is_eq(e2, j);
-          if (e2 + 1 < NCH && live(e2 + 1)) c1 += is_eq(e2 + 1, j);
-        }
-        int gtot;
-        const int gb = block_exclusive_sum<NT>((c1 << 16) | c0, wsum, gtot);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = e2 + h;
-          if (e < NCH && live(e)) {
-            int rank = eq_before_group + (h ? gb >> 16 : gb & 0xFFFF);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (is_eq(e, j)) {
-                if (rank < krem) eqtake |= 1u << (4 * e + j);
-                ++rank;
-              }
-            eq_before_group += h ? gtot >> 16 : gtot & 0xFFFF;
+          const int d = binat(e, j);
+          if (cand_at(e, j) && d >= d1 && d < 2048) {
+            const uint32_t slot = atomicAdd(&hist[d], 0x10000u) >> 16;
+            ord[slot] = ((u64)(~keyof(val[4 * e + j])) << 32) | ((uint32_t)d << 16) | (uint32_t)idx(e, j);
           }
         }
       }
-    }
-    // Selected entries as (~key, bin, index) packed so that ascending order within a bin is
-    // (score descending, index ascending); indices are < 2^16 and bins < 2^11.
-    u64* ord = selA;
-    auto put = [&](int e, int j) {
-      const uint32_t d = (uint32_t)binat(e, j);
-      const uint32_t slot = atomicAdd(&hist[d], 0x10000u) >> 16;
-      ord[slot] = ((u64)(~keyat(e, j)) << 32) | (d << 16) | (uint32_t)idx(e, j);
-    };
-    if (neq > krem) {
-#pragma unroll
-      for (int e = 0; e < NCH; ++e)
-        if (live(e)) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (is_gt(e, j) || (is_eq(e, j) && ((eqtake >> (4 * e + j)) & 1u))) put(e, j);
-        }
-    } else {
-#pragma unroll
-      for (int e = 0; e < NCH; ++e)
-        if (live(e)) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (is_ge(e, j)) put(e, j);
-        }
-    }
     __syncthreads();
-    // ---- each entry's rank inside its bin gives its output position. After the scatter
-    //      the high half of bin d's word is the end of its range; bins above d1 are taken
-    //      whole, bin d1 from a1 on. Two entries per thread at a time, so that their LDS
-    //      reads overlap; a bin is read four entries at a time (reads past its end stay
-    //      inside the workgroup's LDS and are masked out).
+    // ---- each entry's rank inside its bin gives its output position. After the scatter the
+    //      high half of a bin's word is the end of its range (every entry of bins >= d1 was
+    //      placed); bin d1 keeps its first nsel - a1 entries, which takes the lowest indices
+    //      among scores equal to the last one taken. Two entries per thread at a time, so
+    //      that their LDS reads overlap; a bin is read four entries at a time (reads past its
+    //      end stay inside the workgroup's LDS and are masked out).
+    const int krem1 = nsel - a1;
+    const int n_ent = a1 + c1;
     auto store = [&](u64 v, int dest) {
       out.store(dest, f2u(key_score(~(uint32_t)(v >> 32))), (int)((uint32_t)v & 0xFFFFu));
     };
-    for (int i0 = tid; i0 < nsel; i0 += 2 * NT) {
-      const bool two = i0 + NT < nsel;
+    for (int i0 = tid; i0 < n_ent; i0 += 2 * NT) {
+      const bool two = i0 + NT < n_ent;
       const u64 v0 = ord[i0];
       const u64 v1 = two ? ord[i0 + NT] : 0ull;
       const int e0 = (int)(((uint32_t)v0 >> 16) & 2047u), e1 = (int)(((uint32_t)v1 >> 16) & 2047u);
       const uint32_t w0 = hist[e0], w1 = hist[e1];
       const int end0 = (int)(w0 >> 16), end1 = two ? (int)(w1 >> 16) : 0;
-      const int b0 = e0 == d1 ? a1 : end0 - (int)(w0 & 0xFFFFu);
-      const int b1 = two ? (e1 == d1 ? a1 : end1 - (int)(w1 & 0xFFFFu)) : 0;
+      const int b0 = end0 - (int)(w0 & 0xFFFFu);
+      const int b1 = two ? end1 - (int)(w1 & 0xFFFFu) : 0;
       int r0 = 0, r1 = 0;
       for (int q = 0; b0 + q < end0 || b1 + q < end1; q += 4) {
 #pragma unroll
@@ -785,15 +687,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
           r1 += b1 + q + j < end1 && x1 < v1;
         }
       }
-      store(v0, b0 + r0);
-      if (two) store(v1, b1 + r1);
+      if (e0 != d1 || r0 < krem1) store(v0, b0 + r0);
+      if (two && (e1 != d1 || r1 < krem1)) store(v1, b1 + r1);
     }
     out.finish<NT>(a, t, nsel, u);
     return;
   }
 
-  // Rows the bins do not separate (a clustered threshold bin, a selected bin of more than
-  // kBucketMax keys, no finite score range) are left to topk_fallback_kernel, which finds
+  // Rows the bins do not separate (a selected bin of more than kBucketMax keys, the threshold
+  // bin's included, or no finite score range) are left to topk_fallback_kernel, which finds
   // them by this negative length. Finishing them here would double this kernel's registers
   // (fewer rows in flight for every row) to save one launch.
   if (tid == 0) a.out_lengths[t] = -1;
@@ -1034,8 +936,9 @@ int p2_of(int topk, int max_cand) {
 
 }  // namespace
 
-// Dynamic LDS layout: selA [p2max] u64 | hist [kHistSlots] u32 | wsum [32] | misc [16].
-int topk_hist_offset(int max_cand, int topk) { return p2_of(topk, max_cand) * 8; }
+// Dynamic LDS layout: selA [p2max + kBucketMax] u64 (the selection and the rest of the
+// threshold bin) | hist [kHistSlots] u32 | wsum [32] | misc [16].
+int topk_hist_offset(int max_cand, int topk) { return (p2_of(topk, max_cand) + kBucketMax) * 8; }
 
 size_t topk_lds_bytes(int max_cand, int topk) {
   return (size_t)topk_hist_offset(max_cand, topk) + kHistSlots * 4 + 32 * 4 + 16 * 4;
@@ -1078,7 +981,7 @@ hipError_t launch_topk(const ScoreTopkLaunch& p, hipStream_t st) {
     else if (hi <= 2048) e = launch_cfg<256, 8>(a, lds, (int)grid, st);
     else if (hi <= 4096) e = launch_cfg<256, 16>(a, lds, (int)grid, st);
     // Longer rows take more candidates per thread rather than wider workgroups: a
-    // workgroup's serial steps (block reductions, the one-wave threshold ranking) then cost
+    // workgroup's serial steps (block reductions, the histogram scan) then cost
     // fewer waiting waves, and more rows are in flight per CU (measured: 8193-candidate rows
     // 1.5x faster as 256 x 32 than as 1024 x 16).
     else if (hi <= 8192) e = launch_cfg<256, 32>(a, lds, (int)grid, st);
