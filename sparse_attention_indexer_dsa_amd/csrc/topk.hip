@@ -457,6 +457,7 @@ __device__ __forceinline__ bool map_row(const TopkArgs& a, int j, int& t, int& b
     return true;
   }
   if (!CLS) {
+    if (j >= a.T) return false;
     t = j;
   } else {
     const int ulo = a.cls_lo <= 0 ? 0 : a.cls_lo * kp - 1;
