@@ -12,11 +12,13 @@
 // Work decomposition. A workgroup of 4 waves owns one query token and 64 of its heads, one
 // wave per 16 heads; the wave's q operands (16 heads x 576) stay in registers. The row's
 // slots are swept in tiles of 32: the workgroup gathers the 32 selected entries into LDS
-// twice, key-major for the scores (contraction over the 576 elements) and as groups of 8
-// keys per value element for the weighted sum (contraction over keys), so both products
-// read their MFMA operands as 16-byte LDS loads. Entries are read through a buffer
-// descriptor over the latent tensor: an empty slot or an index outside [0, S) reads zeros
-// without touching memory and its score is masked.
+// once, key-major. The scores (contraction over the 576 elements) read their key operands
+// as 16-byte loads; the weighted sum (contraction over keys) reads its value operands with
+// transposing loads (ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + b gets
+// element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lanes
+// addressing 4 keys x 4 column pieces receive 4 consecutive keys of one column each).
+// Entries are read through a buffer descriptor over the latent tensor: an empty slot or an
+// index outside [0, S) reads zeros without touching memory and its score is masked.
 //
 // Softmax: online, in base 2 (scores pre-multiplied by sm_scale * log2 e). The running row
 // maximum is raised only when a tile's maximum exceeds it by more than 8 (then the 128
@@ -40,6 +42,7 @@ namespace dsa {
 namespace {
 
 typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -49,17 +52,14 @@ constexpr int kNK = 32;                        // slots per tile
 constexpr int kKPitch = kRowB + 16;            // key-major LDS row (16-byte skew between keys)
 constexpr int kPPitch = (kNK + 8) * 2;         // weight staging row (one head, 32 keys)
 constexpr int kLdsK = kNK * kKPitch;
-// [key group][value element][8 keys], element c of a group in 16-byte slot c + c/8: a lane's
-// writes (8 consecutive elements per lane) then fall 9 slots apart and the operand reads (16
-// consecutive elements) nearly so, both spread over the banks
-constexpr int kVSlots = kDV + kDV / 8;
-constexpr int kLdsV = (kNK / 8) * kVSlots * 16;
 constexpr int kLdsP = 4 * 16 * kPPitch;
-constexpr int kLdsBytes = kLdsK + kLdsV + kLdsP;
+constexpr int kLdsOut = 4 * 16 * kDV * 2;      // the output staging after the sweep
+constexpr int kLdsBytes = kLdsK + kLdsP > kLdsOut ? kLdsK + kLdsP : kLdsOut;
 constexpr int kSteps = kDK / 32;               // MFMA k-steps of the score product
 constexpr int kVBlocks = kDV / 16;             // 16-column blocks of the value product
 static_assert(kDK % 32 == 0 && kDV % 128 == 0 && kDV < kDK, "entry layout");
-static_assert(4 * 16 * kDV * 2 <= kLdsBytes, "the output staging reuses the tile buffers");
+static_assert(kLdsOut <= kLdsBytes, "the output staging reuses the tile buffers");
+static_assert(kKPitch % 8 == 0, "transposing loads take 8-byte aligned pieces");
 
 struct AttnArgs {
   const uint16_t* q; const uint16_t* kv; const int32_t* indices; const int32_t* lengths;
@@ -92,10 +92,9 @@ __device__ __forceinline__ float row16_sum(float x) {
 __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* kt = smem;                          // [32 keys][kKPitch]
-  uint8_t* vt = smem + kLdsK;                  // [4][kDV][8 keys] bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* pst = smem + kLdsK + kLdsV + wv * 16 * kPPitch;   // this wave's weights [16 heads][32 keys]
+  uint8_t* pst = smem + kLdsK + wv * 16 * kPPitch;   // this wave's weights [16 heads][32 keys]
 
   const int nhb = (a.H + 63) / 64;
   const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
@@ -151,10 +150,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 
   for (int j0 = 0; j0 < n; j0 += kNK) {
     __syncthreads();                           // the previous tile is no longer read
-    // ---- gather. Value part: wave wv takes keys 8wv .. 8wv+7, lane l their 16 bytes of
-    //      elements 8l .. 8l+7, in two halves of 4 keys (fewer registers next to the resident
-    //      operands); the key-major copy is written as loaded and each 4 x 8 block is
-    //      transposed in registers into the grouped layout. The last 64 elements: thread tid
+    // ---- gather. First 512 elements: wave wv takes keys 8wv .. 8wv+7, lane l their 16 bytes
+    //      of elements 8l .. 8l+7, in two halves of 4 keys (fewer registers next to the
+    //      resident operands), written key-major as loaded. The last 64 elements: thread tid
     //      takes key tid/8, piece tid%8, loaded together with the first half.
     const uint32_t vmask = (uint32_t)__ballot(lane < 32 && ixm >= 0 && ixm < a.S);   // valid slots (bit j - j0)
     {
@@ -180,15 +178,6 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           *reinterpret_cast<u32x4*>(kt + (8 * wv + 4 * hf + k) * kKPitch + 16 * lane) = raw[k];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          // element 8*lane + d of the 4 keys: half d%2 of word d/2 of each key's piece
-          uint2 w;
-          const uint32_t a0 = raw[0][d >> 1], a1 = raw[1][d >> 1], a2 = raw[2][d >> 1], a3 = raw[3][d >> 1];
-          w.x = (d & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-          w.y = (d & 1) ? ((a2 >> 16) | (a3 & 0xFFFF0000u)) : ((a2 & 0xFFFFu) | (a3 << 16));
-          *reinterpret_cast<uint2*>(vt + (wv * kVSlots + 9 * lane + d) * 16 + 8 * hf) = w;
-        }
       }
     }
     __syncthreads();
@@ -239,13 +228,18 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- weighted values: A = weights (head r16, keys 8*g4 .. +7), B = values (column
-    //      16c + r16, the same keys)
+    //      16c + r16, the same keys), by two transposing loads from the key-major tile: lane
+    //      r16 of group g4 addresses keys 8*g4 + 4h + r16/4, columns 16c + 4*(r16%4) .. +3
     const u32x4 pv = *reinterpret_cast<const u32x4*>(pst + r16 * kPPitch + 16 * g4);
     const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pv);
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const uint8_t* vrow = kt + (8 * g4 + (r16 >> 2)) * kKPitch + 8 * (r16 & 3);
 #pragma unroll
     for (int c = 0; c < kVBlocks; ++c) {
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(vt + (g4 * kVSlots + 18 * c + r16 + (r16 >> 3)) * 16);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, *reinterpret_cast<const bf16x8*>(&bv), o[c], 0, 0, 0);
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 32 * c));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 4 * kKPitch + 32 * c));
+      const bf16x8 bv = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[c], 0, 0, 0);
     }
   }
 
