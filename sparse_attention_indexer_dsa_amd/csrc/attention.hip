@@ -11,14 +11,20 @@
 //
 // Work decomposition. A workgroup of 4 waves owns one query token and 64 of its heads, one
 // wave per 16 heads; the wave's q operands (16 heads x 576) stay in registers. The row's
-// slots are swept in tiles of 32: the workgroup gathers the 32 selected entries into LDS
-// once, key-major. The scores (contraction over the 576 elements) read their key operands
-// as 16-byte loads; the weighted sum (contraction over keys) reads its value operands with
-// transposing loads (ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + b gets
-// element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lanes
-// addressing 4 keys x 4 column pieces receive 4 consecutive keys of one column each).
-// Entries are read through a buffer descriptor over the latent tensor: an empty slot or an
-// index outside [0, S) reads zeros without touching memory and its score is masked.
+// slots are swept in tiles of 32, each gathered key-major into one of two LDS buffers by
+// direct buffer-to-LDS loads: tile j+1 streams in while tile j is multiplied out, so the
+// gather's memory latency hides behind a tile of work (the entries' indices are read a tile
+// earlier still). An entry's value part (its first 512 elements, 1024 bytes: one load of 64
+// lanes x 16 bytes) lands in a row of its own, rows 16 bytes apart modulo 256; the other 64
+// elements of 8 keys form one load, their 16-byte chunks XOR-swizzled by the key. The scores
+// (contraction over the 576 elements) read their key operands as 16-byte loads; the weighted
+// sum (contraction over keys) reads its value operands with transposing loads
+// (ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + b gets element b of the
+// 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lanes addressing 4 keys x 4
+// column pieces receive 4 keys of one column each). The contraction over keys takes them in
+// an order of its own (kpos below) that makes those loads free of bank conflicts. Entries
+// are read through a buffer descriptor over the latent tensor: an empty slot or an index
+// outside [0, S) reads zeros without touching memory and its score is masked.
 //
 // Softmax: online, in base 2 (scores pre-multiplied by sm_scale * log2 e). The running row
 // maximum is raised only when a tile's maximum exceeds it by more than 8 (then the 128
@@ -48,18 +54,55 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDK = kMlaKeyWidth, kDV = kMlaValueWidth;
 constexpr int kRowB = kDK * 2;                 // bytes per latent entry
+constexpr int kVB = kDV * 2;                   // its value part
+constexpr int kRB = kRowB - kVB;               // the rest (the 64 positional elements)
 constexpr int kNK = 32;                        // slots per tile
-constexpr int kKPitch = kRowB + 16;            // key-major LDS row (16-byte skew between keys)
+constexpr int kVPitch = kVB + 16;              // value-part LDS row (16-byte skew between keys)
+constexpr int kLdsV = kNK * kVPitch;
+constexpr int kLdsTile = kLdsV + kNK * kRB;    // one tile buffer: value parts, then the rest
 constexpr int kPPitch = (kNK + 8) * 2;         // weight staging row (one head, 32 keys)
-constexpr int kLdsK = kNK * kKPitch;
 constexpr int kLdsP = 4 * 16 * kPPitch;
 constexpr int kLdsOut = 4 * 16 * kDV * 2;      // the output staging after the sweep
-constexpr int kLdsBytes = kLdsK + kLdsP > kLdsOut ? kLdsK + kLdsP : kLdsOut;
+constexpr int kLdsBytes = 2 * kLdsTile + kLdsP > kLdsOut ? 2 * kLdsTile + kLdsP : kLdsOut;
 constexpr int kSteps = kDK / 32;               // MFMA k-steps of the score product
+constexpr int kVSteps = kDV / 32;              // ... of them within the value part
 constexpr int kVBlocks = kDV / 16;             // 16-column blocks of the value product
 static_assert(kDK % 32 == 0 && kDV % 128 == 0 && kDV < kDK, "entry layout");
-static_assert(kLdsOut <= kLdsBytes, "the output staging reuses the tile buffers");
-static_assert(kKPitch % 8 == 0, "transposing loads take 8-byte aligned pieces");
+static_assert(kVB == 64 * 16 && kRB == 8 * 16 && kNK == 32, "one direct load per value part; one per 8 keys' rest");
+static_assert(kLdsOut <= kLdsBytes && 2 * kLdsBytes <= 160 * 1024, "two workgroups per CU; output staging reuses the tiles");
+
+// Chunk c (of 8) of the rest of key r sits at c ^ rsw(r): 16 consecutive keys (rows 128 bytes
+// apart) reading one chunk then hit 16 distinct 16-byte slots modulo 256 bytes.
+__device__ __forceinline__ int rsw(int r) { return (r >> 1) & 7; }
+
+// Position in the weighted sum's contraction (MFMA k index) of the tile's key r. Lanes of
+// group g4 of the transposing loads take k = 8 g4 + 4 h + i from key 16 (g4 / 2) + 8 (g4 % 2)
+// + 2 i + h, so the 8 keys that 32 lanes read in one load all have even (h = 0) or all odd
+// (h = 1) rows, whose 32-byte pieces sit at distinct 32-byte slots modulo 256 bytes.
+__device__ __forceinline__ int kpos(int r) { return 8 * (r >> 3) + 4 * (r & 1) + ((r >> 1) & 3); }
+
+// 16 bytes per lane from buffer offset voffset to LDS at lds + 16 * lane (lds wave-uniform).
+// Written as assembly so that the compiler does not see an LDS store in flight: it would
+// otherwise wait for these loads before every LDS read it cannot tell apart from them (the
+// transposing loads among them), which would serialise the gather with the tile before it.
+// The kernel waits for them itself (vmcnt(0) before the barrier that publishes a tile); the
+// compiler's own vmcnt waits only grow stricter from loads it does not count, since loads
+// complete in issue order. M0 (the LDS address of the load) is saved and restored; one wait
+// state separates its write from the load that reads it.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voffset) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(r), "s"(la)
+      : "memory");
+}
 
 struct AttnArgs {
   const uint16_t* q; const uint16_t* kv; const int32_t* indices; const int32_t* lengths;
@@ -91,10 +134,9 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* kt = smem;                          // [32 keys][kKPitch]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* pst = smem + kLdsK + wv * 16 * kPPitch;   // this wave's weights [16 heads][32 keys]
+  uint8_t* pst = smem + 2 * kLdsTile + wv * 16 * kPPitch;   // this wave's weights [16 heads][32 keys]
 
   const int nhb = (a.H + 63) / 64;
   const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
@@ -104,8 +146,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
   const bool active = h0 < a.H;                // wave-uniform: a wave past the heads only gathers
   const int n = a.lengths ? clampi(__ldg(a.lengths + t), 0, a.topk) : a.topk;
   const int32_t* irow = a.indices + (long long)t * a.topk;
-  const int kvbytes = a.S * kRowB;             // the descriptor's end; offsets there read zeros
-  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(a.kv, kvbytes);
+  const uint32_t kvend = (uint32_t)a.S * kRowB; // the descriptor's end; offsets from there read zeros
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(a.kv, (int)kvend);
 
   const int r16 = lane & 15, g4 = lane >> 4;
   // q operands: head h0 + r16, elements 32*ks + 8*g4 .. +7
@@ -125,70 +167,64 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; lsum[i] = 0.f; }
 
-  // Slot indices are read a tile ahead: the 8 value-part keys of this wave (uniform, scalar
-  // registers), the key of this thread's last-64-element piece and the slot of mask lane l%32.
-  const int kr = tid >> 3, pc = tid & 7;
-  int ixv[8], ixr = -1, ixm = -1;
-  // Every load is issued (addresses clamped into the row, slots past n replaced by -1), so
-  // that the wait counts stay exact on every path.
-  auto load_indices = [&](int j0) {
-    const int last = a.topk - 1;
+  // Gather (nothing passes through registers). Lanes l and 32 + l of every wave hold offm, the
+  // byte offset of slot j0 + l's entry in the latent tensor, or the descriptor's end for an
+  // empty slot or an index outside [0, S) (a byte offset below 2^32 even past the end). Wave
+  // wv loads the value parts of keys 8 wv .. 8 wv + 7 (lane l: chunk l) and the rest of
+  // those 8 keys (lane l: key 8 wv + l / 8, LDS chunk l % 8).
+  const int rkey = 8 * wv + (lane >> 3);
+  const uint32_t rchunk = kVB + 16 * ((lane & 7) ^ rsw(rkey));
+  auto slot_ix = [&](int j0) {                // every lane loads (clamped address) ...
+    return __ldg(irow + min(j0 + (lane & 31), a.topk - 1));
+  };
+  auto slot_off = [&](int ix, int j0) -> uint32_t {   // ... then masks
+    return (j0 + (lane & 31) < n && ix >= 0 && ix < a.S) ? (uint32_t)ix * kRowB : kvend;
+  };
+  auto gather = [&](uint32_t offm, int buf) {
+    uint8_t* dst = smem + buf * kLdsTile;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int j = j0 + 8 * wv + k;
-      const int v = __ldg(irow + min(j, last));
-      ixv[k] = j < n ? v : -1;
+      const int key = 8 * wv + k;
+      lds_dma16(rkv, dst + key * kVPitch, (uint32_t)__builtin_amdgcn_readlane((int)offm, key) + 16 * lane);
     }
-    const int vr = __ldg(irow + min(j0 + kr, last));
-    ixr = j0 + kr < n ? vr : -1;
-    const int jm = j0 + (lane & 31);
-    const int vm = __ldg(irow + min(jm, last));
-    ixm = jm < n ? vm : -1;
+    const uint32_t ro = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * rkey, (int)offm);
+    lds_dma16(rkv, dst + kLdsV + wv * 8 * kRB, ro + rchunk);
   };
-  auto off_of = [&](int ix) { return (ix >= 0 && ix < a.S) ? ix * kRowB : kvbytes; };
-  if (n > 0) load_indices(0);
+  // prologue: tile 0 in flight, the indices of tile 1 requested (first used after the wait
+  // for tile 0, so that no wait for them holds up the gather)
+  uint32_t vm_next = 0;
+  int ixn = 0;
+  if (n > 0) {
+    const uint32_t off0 = slot_off(slot_ix(0), 0);
+    gather(off0, 0);
+    vm_next = (uint32_t)__ballot(lane < 32 && off0 != kvend);
+    ixn = slot_ix(kNK);
+  }
 
-  for (int j0 = 0; j0 < n; j0 += kNK) {
-    __syncthreads();                           // the previous tile is no longer read
-    // ---- gather. First 512 elements: wave wv takes keys 8wv .. 8wv+7, lane l their 16 bytes
-    //      of elements 8l .. 8l+7, in two halves of 4 keys (fewer registers next to the
-    //      resident operands), written key-major as loaded. The last 64 elements: thread tid
-    //      takes key tid/8, piece tid%8, loaded together with the first half.
-    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && ixm >= 0 && ixm < a.S);   // valid slots (bit j - j0)
-    {
-      int cv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) cv[k] = ixv[k];
-      const int offr = off_of(ixr);
-      const u32x4 rope = __builtin_amdgcn_raw_buffer_load_b128(rkv, offr == kvbytes ? offr : offr + 2 * kDV + 16 * pc, 0, 0);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 raw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int off = off_of(cv[4 * hf + k]);
-          raw[k] = __builtin_amdgcn_raw_buffer_load_b128(rkv, off == kvbytes ? off : off + 16 * lane, 0, 0);
-        }
-        if (hf == 0) {
-          // the next tile's indices, in flight during this tile (loads complete in order, so
-          // they are issued after the first gathers)
-          load_indices(j0 + kNK);              // past the row: clamped reads, unused
-          *reinterpret_cast<u32x4*>(kt + kr * kKPitch + 2 * kDV + 16 * pc) = rope;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<u32x4*>(kt + (8 * wv + 4 * hf + k) * kKPitch + 16 * lane) = raw[k];
-      }
+  for (int j0 = 0, buf = 0; j0 < n; j0 += kNK, buf ^= 1) {
+    const uint32_t vmask = vm_next;            // valid slots of this tile (bit j - j0)
+    __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of the tile have landed
+    __syncthreads();                           // ... every wave's; the other buffer is no longer read
+    if (j0 + kNK < n) {                        // the next tile streams in during this one
+      const uint32_t offm = slot_off(ixn, j0 + kNK);
+      gather(offm, buf ^ 1);
+      vm_next = (uint32_t)__ballot(lane < 32 && offm != kvend);
+      ixn = slot_ix(j0 + 2 * kNK);             // past the row: a clamped read, unused
     }
-    __syncthreads();
     if (!active) continue;
+    const uint8_t* kvt = smem + buf * kLdsTile;   // value parts [32][kVPitch]
+    const uint8_t* krt = kvt + kLdsV;             // the rest [32][128], chunks swizzled
 
     // ---- scores of 16 heads x 32 keys: lane holds keys r16 (s0) and 16 + r16 (s1), rows 4*g4 + i
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      const u32x4 b0 = *reinterpret_cast<const u32x4*>(kt + r16 * kKPitch + 64 * ks + 16 * g4);
-      const u32x4 b1 = *reinterpret_cast<const u32x4*>(kt + (16 + r16) * kKPitch + 64 * ks + 16 * g4);
+      // elements 32 ks + 8 g4 .. +7 of keys r16 and 16 + r16 (rsw(16 + r16) = rsw(r16))
+      const uint8_t* p0 = ks < kVSteps ? kvt + r16 * kVPitch + 64 * ks + 16 * g4
+                                       : krt + r16 * kRB + 16 * ((4 * (ks - kVSteps) + g4) ^ rsw(r16));
+      const int d1 = ks < kVSteps ? 16 * kVPitch : 16 * kRB;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(p0);
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(p0 + d1);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b0), s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b1), s1, 0, 0, 0);
     }
@@ -214,30 +250,33 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
         for (int c = 0; c < kVBlocks; ++c) o[c][i] *= alpha;
       }
     }
-    // weights (valid slots have finite scores and a finite maximum); bf16 to the staging rows
+    // weights (valid slots have finite scores and a finite maximum); bf16 to the staging rows,
+    // at the keys' contraction positions
+    const int kp0 = kpos(r16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float p0 = v0 ? __builtin_amdgcn_exp2f(x0[i] - m[i]) : 0.f;
       const float p1 = v1 ? __builtin_amdgcn_exp2f(x1[i] - m[i]) : 0.f;
       lsum[i] += p0 + p1;
       uint16_t* prow = reinterpret_cast<uint16_t*>(pst + (4 * g4 + i) * kPPitch);
-      prow[r16] = bf16_bits(p0);
-      prow[16 + r16] = bf16_bits(p1);
+      prow[kp0] = bf16_bits(p0);               // kpos(16 + r16) = 16 + kpos(r16)
+      prow[16 + kp0] = bf16_bits(p1);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- weighted values: A = weights (head r16, keys 8*g4 .. +7), B = values (column
-    //      16c + r16, the same keys), by two transposing loads from the key-major tile: lane
-    //      r16 of group g4 addresses keys 8*g4 + 4h + r16/4, columns 16c + 4*(r16%4) .. +3
+    // ---- weighted values: A = weights (head r16, contraction positions 8*g4 .. +7), B =
+    //      values (column 16c + r16, the same keys), by two transposing loads: lane r16 of
+    //      group g4 addresses key 16*(g4/2) + 8*(g4%2) + 2*(r16/4) + h (positions 8*g4 + 4h +
+    //      r16/4), columns 16c + 4*(r16%4) .. +3
     const u32x4 pv = *reinterpret_cast<const u32x4*>(pst + r16 * kPPitch + 16 * g4);
     const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pv);
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const uint8_t* vrow = kt + (8 * g4 + (r16 >> 2)) * kKPitch + 8 * (r16 & 3);
+    const uint8_t* vlo = kvt + (16 * (g4 >> 1) + 8 * (g4 & 1) + 2 * (r16 >> 2)) * kVPitch + 8 * (r16 & 3);
 #pragma unroll
     for (int c = 0; c < kVBlocks; ++c) {
-      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 32 * c));
-      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 4 * kKPitch + 32 * c));
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 32 * c));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + kVPitch + 32 * c));
       const bf16x8 bv = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[c], 0, 0, 0);
     }
