@@ -15,7 +15,7 @@
 // direct buffer-to-LDS loads: tile j+1 streams in while tile j is multiplied out, so the
 // gather's memory latency hides behind a tile of work (the entries' indices are read a tile
 // earlier still). An entry's value part (its first 512 elements, 1024 bytes: one load of 64
-// lanes x 16 bytes) lands in a row of its own, rows 16 bytes apart modulo 256; the other 64
+// lanes x 16 bytes) lands in a row of its own, rows 32 bytes apart modulo 256; the other 64
 // elements of 8 keys form one load, their 16-byte chunks XOR-swizzled by the key. The scores
 // (contraction over the 576 elements) read their key operands as 16-byte loads; the weighted
 // sum (contraction over keys) reads its value operands with transposing loads
@@ -57,10 +57,10 @@ constexpr int kRowB = kDK * 2;                 // bytes per latent entry
 constexpr int kVB = kDV * 2;                   // its value part
 constexpr int kRB = kRowB - kVB;               // the rest (the 64 positional elements)
 constexpr int kNK = 32;                        // slots per tile
-constexpr int kVPitch = kVB + 16;              // value-part LDS row (16-byte skew between keys)
+constexpr int kVPitch = kVB + 32;              // value-part LDS row (32-byte skew between keys)
 constexpr int kLdsV = kNK * kVPitch;
 constexpr int kLdsTile = kLdsV + kNK * kRB;    // one tile buffer: value parts, then the rest
-constexpr int kPPitch = (kNK + 8) * 2;         // weight staging row (one head, 32 keys)
+constexpr int kPPitch = (kNK + 16) * 2;        // weight staging row (one head, 32 keys; 6 x 16 bytes)
 constexpr int kLdsP = 4 * 16 * kPPitch;
 constexpr int kLdsOut = 4 * 16 * kDV * 2;      // the output staging after the sweep
 constexpr int kLdsBytes = 2 * kLdsTile + kLdsP > kLdsOut ? 2 * kLdsTile + kLdsP : kLdsOut;
@@ -71,15 +71,24 @@ static_assert(kDK % 32 == 0 && kDV % 128 == 0 && kDV < kDK, "entry layout");
 static_assert(kVB == 64 * 16 && kRB == 8 * 16 && kNK == 32, "one direct load per value part; one per 8 keys' rest");
 static_assert(kLdsOut <= kLdsBytes && 2 * kLdsBytes <= 160 * 1024, "two workgroups per CU; output staging reuses the tiles");
 
-// Chunk c (of 8) of the rest of key r sits at c ^ rsw(r): 16 consecutive keys (rows 128 bytes
-// apart) reading one chunk then hit 16 distinct 16-byte slots modulo 256 bytes.
+// LDS banks. A ds_read_b128 serves a wave in 4 cycles of 16 lanes, each cycle the 8-lane
+// blocks b and b ^ 3 (lanes 0-7 with 24-31, 8-15 with 16-23, and so in the upper half); a
+// b64 read (the transposing one included) serves 32 lanes a cycle. 64 banks of 4 bytes.
+// - Score operands (b128), lane (r16, g4) reading element chunk 4 ks + g4 of key r16: with
+//   value rows 1056 bytes apart a cycle's 16 lanes take the 16-byte slots 2 r + c (r = 0..7)
+//   and 2 r + c + 1 (the block of the next g4), all distinct modulo 256 bytes.
+// - The rest of the entry (chunk c of 8 at c ^ rsw(r), rows 128 bytes apart): distinct too.
+// - Weights (b128 reads of rows 96 bytes apart, slots 6 r + g4): distinct.
 __device__ __forceinline__ int rsw(int r) { return (r >> 1) & 7; }
 
-// Position in the weighted sum's contraction (MFMA k index) of the tile's key r. Lanes of
-// group g4 of the transposing loads take k = 8 g4 + 4 h + i from key 16 (g4 / 2) + 8 (g4 % 2)
-// + 2 i + h, so the 8 keys that 32 lanes read in one load all have even (h = 0) or all odd
-// (h = 1) rows, whose 32-byte pieces sit at distinct 32-byte slots modulo 256 bytes.
-__device__ __forceinline__ int kpos(int r) { return 8 * (r >> 3) + 4 * (r & 1) + ((r >> 1) & 3); }
+// Position in the weighted sum's contraction (MFMA k index) of the tile's key r. The lanes
+// of group g4 of the transposing loads take positions k = 8 g4 + 4 h + i (h = 0 for the first
+// load, 1 for the second; i = r16 / 4) from key 16 (g4 / 2) + 8 h + 4 (g4 % 2) + i. The 8
+// keys that 32 lanes read in one load then differ modulo 8, and value rows 32 r bytes apart
+// modulo 256 put their 32-byte pieces at distinct slots.
+__device__ __forceinline__ int kpos(int r) {
+  return 8 * (2 * (r >> 4) + ((r >> 2) & 1)) + 4 * ((r >> 3) & 1) + (r & 3);
+}
 
 // 16 bytes per lane from buffer offset voffset to LDS at lds + 16 * lane (lds wave-uniform).
 // Written as assembly so that the compiler does not see an LDS store in flight: it would
@@ -229,20 +238,20 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b1), s1, 0, 0, 0);
     }
     const bool v0 = (vmask >> r16) & 1u, v1 = (vmask >> (16 + r16)) & 1u;
-    float x0[4], x1[4], mt[4];
+    float x0[4], x1[4];
     bool raise = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x0[i] = v0 ? s0[i] * a.scale_log2 : -INFINITY;
       x1[i] = v1 ? s1[i] * a.scale_log2 : -INFINITY;
-      mt[i] = row16_max(fmaxf(x0[i], x1[i]));
-      raise |= mt[i] > m[i] + 8.f;
+      raise |= fmaxf(x0[i], x1[i]) > m[i] + 8.f;   // m[i] is uniform over the row's 16 lanes
     }
     if (__ballot(raise) != 0ull) {
       // new maxima (every row of the wave, so the decision stays uniform)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mn = fmaxf(m[i], mt[i]);
+        const float mt = row16_max(fmaxf(x0[i], x1[i]));
+        const float mn = fmaxf(m[i], mt);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);   // exp2(-inf) = 0 at the start
         m[i] = mn;
         lsum[i] *= alpha;
@@ -267,17 +276,28 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- weighted values: A = weights (head r16, contraction positions 8*g4 .. +7), B =
     //      values (column 16c + r16, the same keys), by two transposing loads: lane r16 of
-    //      group g4 addresses key 16*(g4/2) + 8*(g4%2) + 2*(r16/4) + h (positions 8*g4 + 4h +
+    //      group g4 addresses key 16*(g4/2) + 8h + 4*(g4%2) + r16/4 (position 8*g4 + 4h +
     //      r16/4), columns 16c + 4*(r16%4) .. +3
     const u32x4 pv = *reinterpret_cast<const u32x4*>(pst + r16 * kPPitch + 16 * g4);
     const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pv);
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const uint8_t* vlo = kvt + (16 * (g4 >> 1) + 8 * (g4 & 1) + 2 * (r16 >> 2)) * kVPitch + 8 * (r16 & 3);
+    const uint8_t* vlo = kvt + (16 * (g4 >> 1) + 4 * (g4 & 1) + (r16 >> 2)) * kVPitch + 8 * (r16 & 3);
+    // loads run kPVAhead column blocks ahead of the products (written in that order: the
+    // scheduler keeps source order where it cannot afford the registers to reorder)
+    constexpr int kPVAhead = 3;
+    v4i16 lo4[kPVAhead], hi4[kPVAhead];
+#pragma unroll
+    for (int c = 0; c < kPVAhead; ++c) {
+      lo4[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 32 * c));
+      hi4[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 8 * kVPitch + 32 * c));
+    }
 #pragma unroll
     for (int c = 0; c < kVBlocks; ++c) {
-      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 32 * c));
-      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + kVPitch + 32 * c));
-      const bf16x8 bv = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 bv = __builtin_shufflevector(lo4[c % kPVAhead], hi4[c % kPVAhead], 0, 1, 2, 3, 4, 5, 6, 7);
+      if (c + kPVAhead < kVBlocks) {
+        lo4[c % kPVAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 32 * (c + kPVAhead)));
+        hi4[c % kPVAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 8 * kVPitch + 32 * (c + kPVAhead)));
+      }
       o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[c], 0, 0, 0);
     }
   }
