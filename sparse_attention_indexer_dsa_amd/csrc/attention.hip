@@ -17,26 +17,27 @@
 // earlier still). An entry's value part (its first 512 elements, 1024 bytes: one load of 64
 // lanes x 16 bytes) lands in a row of its own, rows 32 bytes apart modulo 256; the other 64
 // elements of 8 keys form one load, their 16-byte chunks XOR-swizzled by the key. The scores
-// (contraction over the 576 elements) read their key operands as 16-byte loads; the weighted
-// sum (contraction over keys) reads its value operands with transposing loads
-// (ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + b gets element b of the
-// 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lanes addressing 4 keys x 4
-// column pieces receive 4 keys of one column each). The contraction over keys takes them in
-// an order of its own (kpos below) that makes those loads free of bank conflicts. Entries
-// are read through a buffer descriptor over the latent tensor: an empty slot or an index
-// outside [0, S) reads zeros without touching memory and its score is masked.
+// (contraction over the 576 elements) are formed transposed, S^T = K q^T, with the keys as
+// MFMA rows read by 16-byte loads and the wave's 16 heads as columns, so that a lane ends
+// with one head and 8 of the tile's keys. Those 8 weights are, as they stand, the lane's
+// operand of the weighted sum, also formed transposed (O^T = V^T P^T), whose value operands
+// come from transposing loads (ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + b
+// gets element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lanes
+// addressing 4 keys x 4 column pieces receive 4 keys of one column each). Entries are read
+// through a buffer descriptor over the latent tensor: an empty slot or an index outside
+// [0, S) reads zeros without touching memory and its score is masked.
 //
-// Softmax: online, in base 2 (scores pre-multiplied by sm_scale * log2 e). The running row
-// maximum is raised only when a tile's maximum exceeds it by more than 8 (then the 128
-// accumulator registers are rescaled); otherwise weights up to 2^8 accumulate against the
-// older maximum, which is exact in real arithmetic and keeps the rescale off the common
-// path. Weights enter the value product as bf16 (nearest even); the normaliser sums them in
+// Softmax: online, in base 2 (scores pre-multiplied by sm_scale * log2 e). A head's running
+// maximum (kept by each of its 4 lanes) is raised only when a score exceeds it by more than 8
+// (then the 128 accumulator registers are rescaled); otherwise weights up to 2^8 accumulate
+// against the older maximum, which is exact in real arithmetic and keeps the rescale, and
+// every cross-lane reduction, off the common path. Weights enter the value product as bf16 (nearest even); the normaliser sums them in
 // fp32. Workgroups are numbered so that each XCD (block b runs on XCD b % 8) takes a
 // contiguous range of tokens, whose selections overlap, through its own L2.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 (lane l): A holds row l%16, 8 consecutive k from 8(l/16);
 // B holds column l%16, the same k; the 16x16 fp32 result gives lane l column l%16, rows
-// 4(l/16) .. 4(l/16)+3.
+// 4(l/16) .. 4(l/16)+3. Below r16 = l % 16 and g4 = l / 16.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -51,6 +52,8 @@ typedef short bf16x8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
 constexpr int kDK = kMlaKeyWidth, kDV = kMlaValueWidth;
 constexpr int kRowB = kDK * 2;                 // bytes per latent entry
@@ -60,10 +63,9 @@ constexpr int kNK = 32;                        // slots per tile
 constexpr int kVPitch = kVB + 32;              // value-part LDS row (32-byte skew between keys)
 constexpr int kLdsV = kNK * kVPitch;
 constexpr int kLdsTile = kLdsV + kNK * kRB;    // one tile buffer: value parts, then the rest
-constexpr int kPPitch = (kNK + 16) * 2;        // weight staging row (one head, 32 keys; 6 x 16 bytes)
-constexpr int kLdsP = 4 * 16 * kPPitch;
-constexpr int kLdsOut = 4 * 16 * kDV * 2;      // the output staging after the sweep
-constexpr int kLdsBytes = 2 * kLdsTile + kLdsP > kLdsOut ? 2 * kLdsTile + kLdsP : kLdsOut;
+constexpr int kOPitch = kDV * 2 + 16;          // output staging row (one head)
+constexpr int kLdsOut = 4 * 16 * kOPitch;      // the output staging after the sweep
+constexpr int kLdsBytes = 2 * kLdsTile > kLdsOut ? 2 * kLdsTile : kLdsOut;
 constexpr int kSteps = kDK / 32;               // MFMA k-steps of the score product
 constexpr int kVSteps = kDV / 32;              // ... of them within the value part
 constexpr int kVBlocks = kDV / 16;             // 16-column blocks of the value product
@@ -73,22 +75,16 @@ static_assert(kLdsOut <= kLdsBytes && 2 * kLdsBytes <= 160 * 1024, "two workgrou
 
 // LDS banks. A ds_read_b128 serves a wave in 4 cycles of 16 lanes, each cycle the 8-lane
 // blocks b and b ^ 3 (lanes 0-7 with 24-31, 8-15 with 16-23, and so in the upper half); a
-// b64 read (the transposing one included) serves 32 lanes a cycle. 64 banks of 4 bytes.
-// - Score operands (b128), lane (r16, g4) reading element chunk 4 ks + g4 of key r16: with
+// b64 access (the transposing read included) serves 32 lanes a cycle. 64 banks of 4 bytes.
+// - Key operands (b128), lane (r16, g4) reading element chunk 4 ks + g4 of key r16: with
 //   value rows 1056 bytes apart a cycle's 16 lanes take the 16-byte slots 2 r + c (r = 0..7)
 //   and 2 r + c + 1 (the block of the next g4), all distinct modulo 256 bytes.
 // - The rest of the entry (chunk c of 8 at c ^ rsw(r), rows 128 bytes apart): distinct too.
-// - Weights (b128 reads of rows 96 bytes apart, slots 6 r + g4): distinct.
+// - Value operands (transposing b64): the 32 lanes of groups g4 = 0, 1 (or 2, 3) read 32-byte
+//   pieces of 8 consecutive keys, 32 bytes apart modulo 256: distinct.
+// - Output staging (b64 writes, rows 1040 bytes apart): lane (r16, g4) writes dwords
+//   4 r16 + 2 g4 + {0, 1} modulo 64: distinct over 32 lanes.
 __device__ __forceinline__ int rsw(int r) { return (r >> 1) & 7; }
-
-// Position in the weighted sum's contraction (MFMA k index) of the tile's key r. The lanes
-// of group g4 of the transposing loads take positions k = 8 g4 + 4 h + i (h = 0 for the first
-// load, 1 for the second; i = r16 / 4) from key 16 (g4 / 2) + 8 h + 4 (g4 % 2) + i. The 8
-// keys that 32 lanes read in one load then differ modulo 8, and value rows 32 r bytes apart
-// modulo 256 put their 32-byte pieces at distinct slots.
-__device__ __forceinline__ int kpos(int r) {
-  return 8 * (2 * (r >> 4) + ((r >> 2) & 1)) + 4 * ((r >> 3) & 1) + (r & 3);
-}
 
 // 16 bytes per lane from buffer offset voffset to LDS at lds + 16 * lane (lds wave-uniform).
 // Written as assembly so that the compiler does not see an LDS store in flight: it would
@@ -124,28 +120,10 @@ struct AttnArgs {
 // bf16 bits of x, nearest even (one v_cvt_pk_bf16_f32 on gfx950; the values here are finite).
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
-// Max / sum over the 16 lanes of a DPP row (row rotations; every lane gets the result).
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
-  return x;
-}
-
-__device__ __forceinline__ float row16_sum(float x) {
-  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
-  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
-  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
-  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
-  return x;
-}
-
 __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* pst = smem + 2 * kLdsTile + wv * 16 * kPPitch;   // this wave's weights [16 heads][32 keys]
 
   const int nhb = (a.H + 63) / 64;
   const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
@@ -169,12 +147,10 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
       qa[ks] = *reinterpret_cast<const bf16x8*>(&v);
     }
   }
-  f32x4 o[kVBlocks];
+  f32x4 o[kVBlocks];                           // O^T: head h0 + r16, value columns 16c + 4 g4 + i
 #pragma unroll
   for (int c = 0; c < kVBlocks; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], lsum[4];                         // rows 4*g4 + i: running maximum, lane's weight sum
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; lsum[i] = 0.f; }
+  float m = -INFINITY, lsum = 0.f;             // head h0 + r16: running maximum, this lane's weight sum
 
   // Gather (nothing passes through registers). Lanes l and 32 + l of every wave hold offm, the
   // byte offset of slot j0 + l's entry in the latent tensor, or the descriptor's end for an
@@ -224,64 +200,60 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
     const uint8_t* kvt = smem + buf * kLdsTile;   // value parts [32][kVPitch]
     const uint8_t* krt = kvt + kLdsV;             // the rest [32][128], chunks swizzled
 
-    // ---- scores of 16 heads x 32 keys: lane holds keys r16 (s0) and 16 + r16 (s1), rows 4*g4 + i
+    // ---- scores, transposed: A = keys (row r16 of each 16-key half: elements 32 ks + 8 g4 ..
+    //      +7), B = q (column = head r16). Lane (r16, g4) gets head r16 with keys 4 g4 + i
+    //      (s0) and 16 + 4 g4 + i (s1), i = 0..3.
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      // elements 32 ks + 8 g4 .. +7 of keys r16 and 16 + r16 (rsw(16 + r16) = rsw(r16))
+      // (rsw(16 + r16) = rsw(r16))
       const uint8_t* p0 = ks < kVSteps ? kvt + r16 * kVPitch + 64 * ks + 16 * g4
                                        : krt + r16 * kRB + 16 * ((4 * (ks - kVSteps) + g4) ^ rsw(r16));
       const int d1 = ks < kVSteps ? 16 * kVPitch : 16 * kRB;
       const u32x4 b0 = *reinterpret_cast<const u32x4*>(p0);
       const u32x4 b1 = *reinterpret_cast<const u32x4*>(p0 + d1);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b0), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(&b1), s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&b0), qa[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&b1), qa[ks], s1, 0, 0, 0);
     }
-    const bool v0 = (vmask >> r16) & 1u, v1 = (vmask >> (16 + r16)) & 1u;
+    const uint32_t vb = vmask >> (4 * g4);      // bit i: key 4 g4 + i; bit 16 + i: key 16 + 4 g4 + i
     float x0[4], x1[4];
     bool raise = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x0[i] = v0 ? s0[i] * a.scale_log2 : -INFINITY;
-      x1[i] = v1 ? s1[i] * a.scale_log2 : -INFINITY;
-      raise |= fmaxf(x0[i], x1[i]) > m[i] + 8.f;   // m[i] is uniform over the row's 16 lanes
+      x0[i] = (vb >> i) & 1u ? s0[i] * a.scale_log2 : -INFINITY;
+      x1[i] = (vb >> (16 + i)) & 1u ? s1[i] * a.scale_log2 : -INFINITY;
+      raise |= fmaxf(x0[i], x1[i]) > m + 8.f;   // m is the same in the head's 4 lanes
     }
     if (__ballot(raise) != 0ull) {
-      // new maxima (every row of the wave, so the decision stays uniform)
+      // new maxima (every head of the wave, so the decision stays uniform): over the lane's
+      // 8 keys, then the head's 4 lanes r16 + 16 g4
+      float mt = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])), fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);   // exp2(-inf) = 0 at the start
+      m = mn;
+      lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mt = row16_max(fmaxf(x0[i], x1[i]));
-        const float mn = fmaxf(m[i], mt);
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);   // exp2(-inf) = 0 at the start
-        m[i] = mn;
-        lsum[i] *= alpha;
-#pragma unroll
-        for (int c = 0; c < kVBlocks; ++c) o[c][i] *= alpha;
-      }
+      for (int c = 0; c < kVBlocks; ++c) o[c] *= alpha;
     }
-    // weights (valid slots have finite scores and a finite maximum); bf16 to the staging rows,
-    // at the keys' contraction positions
-    const int kp0 = kpos(r16);
+    // weights (valid slots have finite scores and a finite maximum), as bf16: the B operand of
+    // the weighted sum, contraction positions 8 g4 + i (key 4 g4 + i) and 8 g4 + 4 + i (key
+    // 16 + 4 g4 + i)
+    f32x8 pf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p0 = v0 ? __builtin_amdgcn_exp2f(x0[i] - m[i]) : 0.f;
-      const float p1 = v1 ? __builtin_amdgcn_exp2f(x1[i] - m[i]) : 0.f;
-      lsum[i] += p0 + p1;
-      uint16_t* prow = reinterpret_cast<uint16_t*>(pst + (4 * g4 + i) * kPPitch);
-      prow[kp0] = bf16_bits(p0);               // kpos(16 + r16) = 16 + kpos(r16)
-      prow[16 + kp0] = bf16_bits(p1);
+      pf[i] = (vb >> i) & 1u ? __builtin_amdgcn_exp2f(x0[i] - m) : 0.f;
+      pf[4 + i] = (vb >> (16 + i)) & 1u ? __builtin_amdgcn_exp2f(x1[i] - m) : 0.f;
+      lsum += pf[i] + pf[4 + i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- weighted values: A = weights (head r16, contraction positions 8*g4 .. +7), B =
-    //      values (column 16c + r16, the same keys), by two transposing loads: lane r16 of
-    //      group g4 addresses key 16*(g4/2) + 8h + 4*(g4%2) + r16/4 (position 8*g4 + 4h +
-    //      r16/4), columns 16c + 4*(r16%4) .. +3
-    const u32x4 pv = *reinterpret_cast<const u32x4*>(pst + r16 * kPPitch + 16 * g4);
-    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pv);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, __builtin_convertvector(pf, bf16x8v));
+    // ---- weighted values, transposed: A = values (row = column 16c + r16; contraction
+    //      positions 8 g4 .. +7) by two transposing loads, lanes a + 4j of group g4 addressing
+    //      key 4 g4 + j (first) or 16 + 4 g4 + j (second), columns 16c + 4a .. +3
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const uint8_t* vlo = kvt + (16 * (g4 >> 1) + 4 * (g4 & 1) + (r16 >> 2)) * kVPitch + 8 * (r16 & 3);
+    const uint8_t* vlo = kvt + (4 * g4 + (r16 >> 2)) * kVPitch + 8 * (r16 & 3);
+    const uint8_t* vhi = vlo + 16 * kVPitch;
     // loads run kPVAhead column blocks ahead of the products (written in that order: the
     // scheduler keeps source order where it cannot afford the registers to reorder)
     constexpr int kPVAhead = 3;
@@ -289,43 +261,44 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < kPVAhead; ++c) {
       lo4[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 32 * c));
-      hi4[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 8 * kVPitch + 32 * c));
+      hi4[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vhi + 32 * c));
     }
 #pragma unroll
     for (int c = 0; c < kVBlocks; ++c) {
-      const bf16x8 bv = __builtin_shufflevector(lo4[c % kPVAhead], hi4[c % kPVAhead], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 av = __builtin_shufflevector(lo4[c % kPVAhead], hi4[c % kPVAhead], 0, 1, 2, 3, 4, 5, 6, 7);
       if (c + kPVAhead < kVBlocks) {
         lo4[c % kPVAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 32 * (c + kPVAhead)));
-        hi4[c % kPVAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vlo + 8 * kVPitch + 32 * (c + kPVAhead)));
+        hi4[c % kPVAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vhi + 32 * (c + kPVAhead)));
       }
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[c], 0, 0, 0);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[c], 0, 0, 0);
     }
   }
 
-  // ---- normalise, stage the wave's 16 x 512 bf16 rows in LDS, store them contiguously
-  float inv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float l = row16_sum(lsum[i]);
-    inv[i] = l > 0.f ? 1.f / l : 0.f;
-    if (a.lse && active && r16 == 0)
-      a.lse[(long long)t * a.H + h0 + 4 * g4 + i] = l > 0.f ? (m[i] + log2f(l)) * 0.69314718055994531f : -INFINITY;
-  }
+  // ---- normalise: the head's weight sum over its 4 lanes; stage the wave's 16 x 512 bf16 rows
+  //      in LDS, store them contiguously
+  float l = lsum;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse && active && g4 == 0)
+    a.lse[(long long)t * a.H + h0 + r16] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
   __syncthreads();                             // every wave is done with the tile buffers
   if (!active) return;
-  uint8_t* ost = smem + wv * 16 * kDV * 2;
+  uint8_t* ost = smem + wv * 16 * kOPitch;
 #pragma unroll
-  for (int c = 0; c < kVBlocks; ++c)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      reinterpret_cast<uint16_t*>(ost + (4 * g4 + i) * kDV * 2)[16 * c + r16] = bf16_bits(o[c][i] * inv[i]);
+  for (int c = 0; c < kVBlocks; ++c) {
+    const f32x4 v = o[c] * inv;
+    const uint64_t pk = (uint64_t)bf16_bits(v[0]) | (uint64_t)bf16_bits(v[1]) << 16 |
+                        (uint64_t)bf16_bits(v[2]) << 32 | (uint64_t)bf16_bits(v[3]) << 48;
+    *reinterpret_cast<uint64_t*>(ost + r16 * kOPitch + 2 * (16 * c + 4 * g4)) = pk;
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint4* dst = reinterpret_cast<uint4*>(a.out + ((long long)t * a.H + h0) * kDV);
 #pragma unroll
-  for (int r = 0; r < 16 * kDV * 2 / 16 / 64; ++r)
-    dst[r * 64 + lane] = reinterpret_cast<const uint4*>(ost)[r * 64 + lane];
+  for (int r = 0; r < 16; ++r)                 // row r: head h0 + r, 64 lanes x 16 bytes
+    dst[r * 64 + lane] = *reinterpret_cast<const uint4*>(ost + r * kOPitch + 16 * lane);
 }
 
 }  // namespace
