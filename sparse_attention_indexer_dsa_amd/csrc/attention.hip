@@ -204,16 +204,24 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
     //      +7), B = q (column = head r16). Lane (r16, g4) gets head r16 with keys 4 g4 + i
     //      (s0) and 16 + 4 g4 + i (s1), i = 0..3.
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    auto key_op = [&](int ks, int half) -> u32x4 {
+      // (rsw(16 + r16) = rsw(r16))
+      const uint8_t* p = ks < kVSteps ? kvt + (16 * half + r16) * kVPitch + 64 * ks + 16 * g4
+                                      : krt + (16 * half + r16) * kRB + 16 * ((4 * (ks - kVSteps) + g4) ^ rsw(r16));
+      return *reinterpret_cast<const u32x4*>(p);
+    };
+    // loads kSAhead steps ahead of their products, the order pinned step by step (the
+    // scheduler would otherwise keep only about two loads in flight)
+    constexpr int kSAhead = 2;
+    u32x4 kb0[kSteps], kb1[kSteps];
+#pragma unroll
+    for (int ks = 0; ks < kSAhead; ++ks) { kb0[ks] = key_op(ks, 0); kb1[ks] = key_op(ks, 1); }
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      // (rsw(16 + r16) = rsw(r16))
-      const uint8_t* p0 = ks < kVSteps ? kvt + r16 * kVPitch + 64 * ks + 16 * g4
-                                       : krt + r16 * kRB + 16 * ((4 * (ks - kVSteps) + g4) ^ rsw(r16));
-      const int d1 = ks < kVSteps ? 16 * kVPitch : 16 * kRB;
-      const u32x4 b0 = *reinterpret_cast<const u32x4*>(p0);
-      const u32x4 b1 = *reinterpret_cast<const u32x4*>(p0 + d1);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&b0), qa[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&b1), qa[ks], s1, 0, 0, 0);
+      if (ks + kSAhead < kSteps) { kb0[ks + kSAhead] = key_op(ks + kSAhead, 0); kb1[ks + kSAhead] = key_op(ks + kSAhead, 1); }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&kb0[ks]), qa[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&kb1[ks]), qa[ks], s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     const uint32_t vb = vmask >> (4 * g4);      // bit i: key 4 g4 + i; bit 16 + i: key 16 + 4 g4 + i
     float x0[4], x1[4];
