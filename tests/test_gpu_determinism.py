@@ -1,4 +1,5 @@
-"""Bit-exact replays and graph capture (GPU).
+"""Bit-exact replays and graph capture (GPU), for the indexer step and the two kernels after the
+selection (softmax over the selection, sparse attention).
 
 Three runs of the same inputs, the second with a concurrent contention stream, must give
 byte-identical operands and outputs (Megatron-LM PR 8403, codex review finding 3: replays
@@ -113,3 +114,81 @@ def test_graph_replay_with_new_boundaries():
             for k in outs:
                 assert torch.equal(outs[k], want[i][k]), (rep, i, k)
             _ = torch.randn(1000, device="cuda").sum().item()    # eager work between replays
+
+
+def _after_selection_inputs(seed):
+    """A small selection (two documents, fp8 indexer with LN + RoPE, top-64), its softmax
+    input, and attention operands drawn beside it (64 heads, 576-wide latent entries)."""
+    import torch
+    inp = gen.small(seed, [300, 212], 64, 128, layernorm=True, rope_dim=64)
+    inp["H"], inp["D"] = 64, 128
+    cfg = dict(precision="fp8", preprocess=True, layernorm=True, rope_dim=64, rope_fp32=True)
+    g = parity.gpu_pipeline(inp, cfg, 64, keep_device=True)
+    T = g["indices"].shape[0]
+    gen_t = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn((T, 64, 576), generator=gen_t, device="cuda").to(torch.bfloat16)
+    kv = torch.randn((T, 576), generator=gen_t, device="cuda").to(torch.bfloat16)
+    return g, q, kv
+
+
+def test_softmax_and_attention_bit_exact():
+    # the two kernels after the selection: three runs, the second beside a contention stream,
+    # byte-identical (fixed reduction orders, no floating-point atomics)
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    g, q, kv = _after_selection_inputs(11)
+    runs = []
+    for rep in range(3):
+        if rep == 1:
+            side = torch.cuda.Stream()
+            a = torch.randn(4096, 4096, device="cuda")
+            with torch.cuda.stream(side):
+                for _ in range(4):
+                    a = a @ a
+                    a = a / a.abs().max()
+        p = dsa.selection_softmax(g["scores"])
+        out, lse = dsa.sparse_attention(q, kv, g["indices"], sm_scale=576 ** -0.5, lengths=g["lengths"])
+        torch.cuda.synchronize()
+        runs.append((p.clone(), out.clone(), lse.clone()))
+    for r in runs[1:]:
+        for x, y in zip(runs[0], r):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def test_softmax_and_attention_graph_replays():
+    # captured once, replayed with eager work and synchronisation between replays; every
+    # replay equals the eager result
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    g, q, kv = _after_selection_inputs(12)
+    T = q.shape[0]
+    p_out = torch.empty_like(g["scores"])
+    o_out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device="cuda")
+    l_out = torch.empty((T, 64), dtype=torch.float32, device="cuda")
+
+    def step():
+        dsa.selection_softmax(g["scores"], out=p_out)
+        dsa.sparse_attention(q, kv, g["indices"], sm_scale=576 ** -0.5, lengths=g["lengths"], out=o_out, lse=l_out)
+
+    step()
+    torch.cuda.synchronize()
+    want = (p_out.clone(), o_out.clone(), l_out.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (p_out, l_out):
+            t.fill_(float("nan"))
+        o_out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip((p_out, o_out, l_out), want):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), rep
+        _ = torch.randn(1000, device="cuda").sum().item()    # eager work between replays
