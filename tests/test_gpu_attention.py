@@ -108,6 +108,7 @@ def _run(q, kv, idx, lens, sm):
     (8, 128, 1000, 7, True),
     (11, 64, 64, 1, False),        # one slot
     (5, 32, 2000, 512, True),      # many tiles
+    (3, 64, 6000, 2048, False),    # 64 tiles: the two gather buffers alternate 32 times
 ])
 def test_random_selections(T, H, S, topk, lengths):
     sm = 1.0 / np.sqrt(DK)
