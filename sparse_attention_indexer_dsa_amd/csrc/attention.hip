@@ -75,10 +75,10 @@ static_assert(kVB == 64 * 16 && kRB == 8 * 16 && kNK == 32, "one direct load per
 static_assert(kLdsOut <= kLdsBytes && 2 * kLdsBytes <= 160 * 1024, "two workgroups per CU; output staging reuses the tiles");
 
 // LDS banks (measured on the device with one access pattern per kernel and the bank-conflict
-// counter). A ds_read_b128 serves a wave in 4 cycles of 16 lanes: lanes 0-7 share a cycle with
-// lanes 24-31 and with no other 8-lane block, and the layouts below assume the same pairing
-// b with b ^ 3 for the other blocks (8-15 with 16-23, and so in the upper half). A b64 access
-// (the transposing read included) serves 32 lanes a cycle. 64 banks of 4 bytes.
+// counter). A ds_read_b128 serves a wave in 4 cycles of 16 lanes, each cycle the 8-lane blocks
+// b and b ^ 3 (lanes 0-7 with 24-31, 8-15 with 16-23, 32-39 with 56-63, 40-47 with 48-55;
+// every other pairing of blocks was seen not to collide). A b64 access (the transposing read
+// included) serves 32 lanes a cycle. 64 banks of 4 bytes.
 // - Key operands (b128), lane (r16, g4) reading element chunk 4 ks + g4 of key r16: with
 //   value rows 1056 bytes apart a cycle's 16 lanes take the 16-byte slots 2 r + c (r = 0..7)
 //   and 2 r + c + 1 (the block of the next g4), all distinct modulo 256 bytes.
