@@ -37,9 +37,11 @@
 // (then the 128 accumulator registers are rescaled); otherwise weights up to 2^8 accumulate
 // against the older maximum, which is exact in real arithmetic and keeps the rescale, and
 // every cross-lane reduction, off the common path. Weights enter the value product as bf16
-// (nearest even); the normaliser sums them in fp32. Workgroups are numbered so that each XCD
-// (block b runs on XCD b % 8) takes a contiguous range of tokens, whose selections overlap,
-// through its own L2.
+// (nearest even); the normaliser sums them in fp32. Workgroups are numbered so that groups of
+// kTokGroup consecutive tokens, whose selections overlap, go to the XCDs in turn (block b runs
+// on XCD b % 8): the workgroups in flight on an XCD share entries through its L2, and every XCD
+// gets tokens from all positions of the documents (a causal row's slot count grows with its
+// position, so contiguous eighths of the tokens would give the XCDs unequal work).
 //
 // MFMA v_mfma_f32_16x16x32_bf16 (lane l): A holds row l%16, 8 consecutive k from 8(l/16);
 // B holds column l%16, the same k; the 16x16 fp32 result gives lane l column l%16, rows
@@ -66,6 +68,7 @@ constexpr int kRowB = kDK * 2;                 // bytes per latent entry
 constexpr int kVB = kDV * 2;                   // its value part
 constexpr int kRB = kRowB - kVB;               // the rest (the 64 positional elements)
 constexpr int kNK = 32;                        // slots per tile
+constexpr int kTokGroup = 64;                  // consecutive tokens per XCD turn
 constexpr int kVPitch = kVB + 32;              // value-part LDS row (32-byte skew between keys)
 constexpr int kLdsV = kNK * kVPitch;
 constexpr int kLdsTile = kLdsV + kNK * kRB;    // one tile buffer: value parts, then the rest
@@ -126,7 +129,7 @@ struct AttnArgs {
   const uint16_t* q; const uint16_t* kv; const int32_t* indices; const int32_t* lengths;
   int T, H, S, topk;
   float scale_log2;      // sm_scale * log2(e)
-  int tper;              // tokens per XCD range
+  int tper;              // tokens per XCD (whole groups)
   uint16_t* out; float* lse;
 };
 
@@ -140,7 +143,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(AttnArgs a) {
 
   const int nhb = (a.H + 63) / 64;
   const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
-  const int t = xcd * a.tper + seq / nhb;
+  const int loc = seq / nhb;                   // the XCD's loc-th token
+  const int t = ((loc / kTokGroup) * 8 + xcd) * kTokGroup + loc % kTokGroup;
   if (t >= a.T) return;                        // whole workgroup
   const int h0 = (seq % nhb) * 64 + 16 * wv;   // this wave's heads (scores, softmax)
   const int e = wv & 1;                        // its half of the value columns
@@ -380,7 +384,7 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
   a.q = q; a.kv = kv; a.indices = indices; a.lengths = lengths;
   a.T = T; a.H = H; a.S = S; a.topk = topk;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.tper = (T + 7) / 8;
+  a.tper = (((T + kTokGroup - 1) / kTokGroup + 7) / 8) * kTokGroup;
   a.out = out; a.lse = lse;
   const int nhb = (H + 63) / 64;
   const long long blocks = 8ll * a.tper * nhb;
