@@ -546,14 +546,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_num_sgpr(82))) void topk_
 #pragma unroll
     for (int e = 0; e < NCH; ++e) {
       if (!live(e)) continue;
+      if (full(e)) {                             // (uniform) no slot past the row
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
-        val[4 * e + j] = v;
-        const float m = idx(e, j) < cand ? v : NAN;
-        vlo = fminf(vlo, m);
-        vhi = fmaxf(vhi, m);
-        fin = __builtin_fmaf(v, 0.f, fin);
+        for (int j = 0; j < 4; ++j) {
+          const float v = u2f(raw[e][j]) + 0.0f;   // -0 + 0 = +0
+          val[4 * e + j] = v;
+          vlo = fminf(vlo, v);
+          vhi = fmaxf(vhi, v);
+          fin = __builtin_fmaf(v, 0.f, fin);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = u2f(raw[e][j]) + 0.0f;
+          val[4 * e + j] = v;
+          const float m = idx(e, j) < cand ? v : NAN;
+          vlo = fminf(vlo, m);
+          vhi = fmaxf(vhi, m);
+          fin = __builtin_fmaf(v, 0.f, fin);
+        }
       }
     }
   }
@@ -645,19 +656,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_num_sgpr(82))) void topk_
     for (int i = tid; i < kHistSlots / 4; i += NT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) { misc[6] = 0; misc[8] = 2047; }
     __syncthreads();
+    // (a group with no slot past the row skips the per-slot test: uniform branch)
+    auto bin_slot = [&](int e, int j, bool inside) {
+      int d = 2048 + (tid & 15);
+      if (inside) {
+        if constexpr (KEEP) d = lvl == 0 ? bin1(val[4 * e + j])
+                                         : (binA[4 * e + j] >= dex ? bin2(val[4 * e + j]) : d);
+        else d = binof(val[4 * e + j]);
+      }
+      if constexpr (KEEP) binA[4 * e + j] = d;
+      atomicAdd(&hist[d], 1u);
+    };
 #pragma unroll
     for (int e = 0; e < NCH; ++e)
       if (live(e)) {
+        if (full(e)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int d = 2048 + (tid & 15);
-          if (in(e, j)) {
-            if constexpr (KEEP) d = lvl == 0 ? bin1(val[4 * e + j])
-                                             : (binA[4 * e + j] >= dex ? bin2(val[4 * e + j]) : d);
-            else d = binof(val[4 * e + j]);
-          }
-          if constexpr (KEEP) binA[4 * e + j] = d;
-          atomicAdd(&hist[d], 1u);
+          for (int j = 0; j < 4; ++j) bin_slot(e, j, true);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bin_slot(e, j, idx(e, j) < cand);
         }
       }
     __syncthreads();
