@@ -117,6 +117,16 @@ def test_random_selections(T, H, S, topk, lengths):
     _check(qd, kvd, idx, lens, sm, out, lse, range(T))
 
 
+def test_token_groups_across_xcds():
+    # 1000 tokens: 16 groups of 64 consecutive tokens dealt to the XCDs in turn, the last one
+    # ragged (40 tokens), with 128 heads (two workgroups per token); rows sampled from every group
+    sm = 1.0 / np.sqrt(DK)
+    T = 1000
+    q, kv, idx, lens = _case(T, 128, 3000, 64, 4242, lengths=True)
+    qd, kvd, out, lse = _run(q, kv, idx, lens, sm)
+    _check(qd, kvd, idx, lens, sm, out, lse, sorted(set(range(0, T, 7)) | {63, 64, 959, 960, T - 1}))
+
+
 def test_edge_rows():
     # every slot empty, all lengths 0, S = 0, and a large score range (weights far below the max)
     sm = 0.05
