@@ -105,6 +105,7 @@ def _run(q, kv, idx, lens, sm):
     (9, 16, 40, 32, False),        # one tile; three of four waves idle (H = 16)
     (13, 64, 300, 100, True),      # ragged last tile, supplied lengths
     (17, 80, 500, 33, False),      # heads past 64: a second workgroup per token with one wave
+    (21, 48, 700, 96, True),       # the second wave pair half past the heads (its other wave idle)
     (8, 128, 1000, 7, True),
     (11, 64, 64, 1, False),        # one slot
     (5, 32, 2000, 512, True),      # many tiles
